@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Attention-forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = the whole hot path over one batch of synthetic input: for the
+default workload (bf16, B=4 H=16 Nq=Nk=4096 d=128, mixed hardware/software
+exp2, tau=8) a non-causal launch followed by a causal launch, each a full
+pass of load -> QK^T -> mask -> lagging-max softmax -> PV -> epilogue.
+Inputs are resident in HBM before timing starts. Throughput counts
+4*B*H*Nq*Nk*d FLOPs per non-causal launch and half that per causal launch.
+
+Prints ONE JSON line. Besides the contract fields it carries
+  roofline      for the dominant kernel (the non-causal launch): algorithmic
+                FLOPs per launch / its mean duration from HIP events recorded
+                on the launch stream inside the timed region, against the
+                dense bf16 MFMA peak of MI355X (2.5 PFLOP/s)
+  cpu_baseline  the float64 oracle timed on a bounded sample of the same
+                workload on the host cores (rank 0, N=1 only)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}   # MI355X dense MFMA, published
+MODE_CODES = {"hw": 0, "emu": 1, "mix": 2}
+DEFAULT_WORKLOAD = "bf16_b4h16_n4096_d128"
+# Measured HBM-traffic calibration (rocprofv3 FETCH_SIZE / WRITE_SIZE on a plain
+# copy of known size, and on the non-causal kernel at the default workload);
+# None until a counter run has been taken for the kernel as it stands.
+TRAFFIC_BYTES_PER_LAUNCH = None
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--exp2-mode", default=None, help="override the workload's exp2 mode (hw, emu, mix, mixK)")
+    p.add_argument("--tau", type=float, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="also run one plain device copy of this many MiB (HBM counter calibration)")
+    return p.parse_args()
+
+
+def flops_of(w, causal: bool) -> float:
+    f = 4.0 * w.B * w.H * w.Nq * w.Nk * w.d
+    return f / 2 if causal else f
+
+
+def cpu_baseline(w, causal_modes):
+    """The float64 oracle, untuned, on one batch entry's heads of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from attn_inputs import make_inputs
+    from oracle import attention_f64
+
+    heads = min(w.H, 16)
+    x = make_inputs(w, B=1, H=heads)
+    flops = 0.0
+    t0 = time.perf_counter()
+    for causal in causal_modes:
+        attention_f64(x["q64"], x["k64"], x["v64"], causal=causal)
+        f = 4.0 * heads * w.Nq * w.Nk * w.d
+        flops += f / 2 if causal else f
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"B=1 H={heads} of the workload (Nq=Nk={w.Nq}, d={w.d}), causal modes {list(causal_modes)}; "
+                  f"float64 numpy, one-shot softmax, full S computed even when causal; {dt:.1f} s",
+        "seconds": round(dt, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the attention forward "
+              f"shards over (batch, head) with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import online_softmax_fwd_amd as attn
+    from attn_inputs import WORKLOADS, make_inputs
+
+    if not os.path.exists(attn.lib_path()):
+        from online_softmax_fwd_amd import build
+        build.build_library(verbose=False)
+    lib = attn.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    w = WORKLOADS[args.workload]
+    mode = args.exp2_mode or w.exp2_mode
+    tau = w.tau if args.tau is None else args.tau
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    x = make_inputs(w)
+    if w.dtype == "bf16":
+        q, k, v = (torch.from_numpy(x[n].view(np.int16)).to(dev).view(torch.bfloat16) for n in ("q", "k", "v"))
+        scales = {}
+    elif w.dtype == "f32":
+        q, k, v = (torch.from_numpy(x[n]).to(dev) for n in ("q", "k", "v"))
+        scales = {}
+    else:
+        q, k, v = (torch.from_numpy(x[n]).to(dev) for n in ("q", "k", "v"))
+        scales = dict(q_scale=torch.from_numpy(x["qs"]).to(dev), k_scale=torch.from_numpy(x["ks"]).to(dev),
+                      v_scale=torch.from_numpy(x["vs"]).to(dev))
+    del x
+    odt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    outs = {c: (torch.empty((w.B, w.H, w.Nq, w.d), dtype=odt, device=dev),
+                torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)) for c in w.causal}
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(causal):
+        o, l = outs[causal]
+        attn.fwd(q, k, v, causal=causal, exp2_mode=mode, tau=tau, out=o, lse=l, stream=stream, **scales)
+
+    for _ in range(args.warmup):
+        for c in w.causal:
+            launch(c)
+    torch.cuda.synchronize()
+
+    # timed region: K steps; per-launch event pairs on the launch stream
+    ev = {c: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for c in w.causal}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        for c in w.causal:
+            ev[c][i][0].record(stream)
+            launch(c)
+            ev[c][i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    per = {c: [a.elapsed_time(b) for a, b in ev[c]] for c in w.causal}
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    step_flops = sum(flops_of(w, c) for c in w.causal)
+    ms_per_step = total_ms / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    dom = False if False in w.causal else w.causal[0]
+    dom_ms = float(np.mean(per[dom]))
+    achieved = flops_of(w, dom) / (dom_ms * 1e-3) / 1e12
+    per_mode = {("causal" if c else "noncausal"): {
+        "ms_mean": round(float(np.mean(per[c])), 4), "ms_min": round(float(np.min(per[c])), 4),
+        "ms_median": round(float(np.median(per[c])), 4),
+        "tflops": round(flops_of(w, c) / (float(np.mean(per[c])) * 1e-3) / 1e12, 2),
+        "pct_of_peak": round(100.0 * flops_of(w, c) / (float(np.mean(per[c])) * 1e-3) / 1e12 / peak, 2),
+    } for c in w.causal}
+
+    mix16 = None
+    if mode == "mix":
+        dcode = {"f32": 0, "bf16": 1, "mxfp8": 2}[w.dtype]
+        mix16 = {("causal" if c else "noncausal"): lib.attn_mix_sixteenths(dcode, w.d, int(c)) for c in w.causal}
+
+    result = {
+        "metric": "attn fwd TFLOP/s, bf16 d=128 N=4096 (causal & non), % of MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "e4m3+e8m0"}[w.dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": f"attention forward {w.name}: {w.dtype} B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d}, "
+                        f"{' + '.join('causal' if c else 'non-causal' for c in w.causal)} per step, "
+                        f"exp2 {mode}, tau={tau}",
+            "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": list(w.causal),
+            "exp2_mode": mode, "mix_sixteenths": mix16, "tau": tau, "seed": w.seed,
+        },
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "per_mode": per_mode,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": f"fwd_{w.dtype}_kernel (d={w.d}, {'causal' if dom else 'non-causal'})",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": TRAFFIC_BYTES_PER_LAUNCH,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, w.causal)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) attention forward library, libattn.so.
+ *
+ * The library computes, for every batch b, head h and query row i,
+ *
+ *     O[b,h,i,:] = softmax_j( scale * Q[b,h,i,:] . K[b,h,j,:] ) V[b,h,j,:]
+ *     LSE[b,h,i] = ln sum_j exp( scale * Q[b,h,i,:] . K[b,h,j,:] )
+ *
+ * with the causal option removing every key j > i before the softmax (top-left
+ * aligned: row i sees keys 0..i). Sources: "Flash Attention 4 -- the algorithm
+ * and the two-MMA problem" (the attention formula, the online-softmax update and
+ * deferred normalisation, the exp2 fold); "Lecture 2 -- Online Softmax and
+ * Numerical Correctness" (safe softmax, the LSE side output, the causal rule);
+ * "FlashAttention-4's Softmax Tricks" (the lagging-max threshold tau and the
+ * degree-3 software exp2). S and P are never written to memory: the kernels
+ * stream K and V in tiles with a running max, denominator and accumulator.
+ *
+ * Conventions for every entry point
+ *   - Pointers named Q, K, V, O, LSE, *_scale, x, y are DEVICE pointers (HIP
+ *     device memory, e.g. from torch). The caller owns all memory; the library
+ *     allocates nothing and keeps no state between calls except the thread-local
+ *     error message.
+ *   - Layout: Q [B,H,Nq,d], K and V [B,H,Nk,d], O [B,H,Nq,d], all contiguous with
+ *     d innermost. LSE [B,H,Nq] float32. Every tensor pointer must be 16-byte
+ *     aligned.
+ *   - Launches are asynchronous on the given stream (NULL = the null stream);
+ *     no call synchronises. On success every element of O and LSE has been
+ *     written once the stream reaches that point.
+ *   - Validation happens before any HIP call; on a validation error nothing is
+ *     launched and nothing is written. A non-zero status leaves a message for
+ *     attn_last_error().
+ *   - Reentrant: concurrent calls on different streams are independent.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (0 = success, negative = error). */
+enum {
+  ATTN_OK = 0,
+  ATTN_E_NULLPTR = -1,   /* a required pointer is NULL                               */
+  ATTN_E_SHAPE = -2,     /* B, H, Nq < 0; Nk < 1 with work to do; sizes too large;
+                            MXFP8 with Nq or Nk not a multiple of 32                   */
+  ATTN_E_HEADDIM = -3,   /* d not supported for the dtype (f32/bf16: 64 or 128;
+                            MXFP8: 128)                                                */
+  ATTN_E_DTYPE = -4,     /* unknown dtype code                                         */
+  ATTN_E_EXP2MODE = -5,  /* unknown exp2_mode                                          */
+  ATTN_E_TAU = -6,       /* tau negative, above 64 or not finite                       */
+  ATTN_E_SCALE = -7,     /* scale not finite or <= 0                                   */
+  ATTN_E_ALIGN = -8,     /* a tensor pointer is not 16-byte aligned                    */
+  ATTN_E_HIP = -9        /* a HIP launch failed (message has the HIP error string)     */
+};
+
+/* Input dtypes. O is float32 for ATTN_F32 and bf16 for ATTN_BF16 and MXFP8. */
+enum {
+  ATTN_F32 = 0,          /* Q, K, V, O float32                                         */
+  ATTN_BF16 = 1,         /* Q, K, V, O bfloat16                                        */
+  ATTN_MXFP8_E4M3 = 2    /* Q, K, V OCP e4m3 bytes plus one E8M0 scale byte per 32x32
+                            block ([B,H,N/32,d/32] uint8, V blocked along the sequence
+                            with the same square blocks); O bfloat16. Source: "PyTorch
+                            FlashAttention-4 adds MXFP8 block-scaled forward and backward
+                            for Blackwell", section "Quantization along both axes and
+                            jagged tensors"                                             */
+};
+
+/*
+ * exp2 of the per-score probabilities P = 2^(S*scale*log2(e) - m*scale*log2(e)):
+ *   ATTN_EXP2_HW   the hardware exponential (v_exp_f32)
+ *   ATTN_EXP2_EMU  the degree-3 software exp2 for every P ("FlashAttention-4's
+ *                  Softmax Tricks", section "The emulated exp2": clamp at -127,
+ *                  split into floor and fraction, 3-FMA Horner polynomial, integer
+ *                  add of floor into the exponent bits)
+ *   ATTN_EXP2_MIX  a fixed share of each lane's P through the software exp2 and the
+ *                  rest through the hardware one; the share comes from the library's
+ *                  tuning table keyed by (dtype, d, causal)
+ *   ATTN_EXP2_MIX_BASE + k (k = 0..16)  the same with exactly k of every 16 P
+ *                  emulated (for tuning sweeps)
+ * The rescale factor and the LSE logarithm always use the hardware units.
+ */
+enum {
+  ATTN_EXP2_HW = 0,
+  ATTN_EXP2_EMU = 1,
+  ATTN_EXP2_MIX = 2,
+  ATTN_EXP2_MIX_BASE = 16
+};
+
+/*
+ * attn_fwd -- bf16 attention forward on the null stream.
+ *
+ *   Q, K, V   device bf16, [B,H,Nq,d] / [B,H,Nk,d] / [B,H,Nk,d]
+ *   O         device bf16 [B,H,Nq,d] (written)
+ *   LSE       device float32 [B,H,Nq] (written): natural-log log-sum-exp of the
+ *             scaled scores of each row
+ *   B, H, Nq  >= 0 (a zero means there is nothing to do: returns ATTN_OK)
+ *   Nk        >= 1 when B*H*Nq > 0
+ *   d         64 or 128
+ *   causal    0 or 1 (top-left aligned mask, key j > query i removed)
+ *   scale     > 0 and finite; multiplies Q.K (1/sqrt(d) for standard attention)
+ *   exp2_mode ATTN_EXP2_* above
+ *   tau       lagging-max threshold in log2 units of the scaled scores
+ *             ("FlashAttention-4's Softmax Tricks", section "Conditional
+ *             rescaling, and when it's exact"): O and the denominator are rescaled
+ *             only when the row max grows by more than tau; 0 <= tau <= 64
+ *             (P stays below 2^tau, far inside float32 and bf16 range)
+ */
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+             int B, int H, int Nq, int Nk, int d, int causal, float scale,
+             int exp2_mode, float tau);
+
+/*
+ * attn_fwd_ex -- attn_fwd with an explicit dtype, MX scales and stream.
+ *
+ *   dtype     ATTN_F32, ATTN_BF16 or ATTN_MXFP8_E4M3
+ *   q_scale, k_scale, v_scale
+ *             device uint8 E8M0 bytes, [B,H,Nq/32,d/32] and [B,H,Nk/32,d/32];
+ *             required for ATTN_MXFP8_E4M3, ignored (may be NULL) otherwise
+ *   stream    a hipStream_t (e.g. torch.cuda.current_stream().cuda_stream), or NULL
+ * For MXFP8, P is re-quantised to e4m3 per 32 keys with an E8M0 scale taken from
+ * that block's score maximum, so a lagging max cannot saturate P (the failure
+ * "FlashAttention-4's Softmax Tricks" describes in "Where 'exact' breaks: P in
+ * FP8" needs a fixed per-tensor P scale); tau = 0, the setting that page gives
+ * for FP8, is the usual choice.
+ */
+int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                int exp2_mode, float tau, int dtype,
+                const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                void* stream);
+
+/*
+ * attn_fwd_stats -- attn_fwd_ex that also counts lagging-max rescale events.
+ *
+ *   stats     device uint64 [4], accumulated into (the caller zeroes it):
+ *             [0] row-block steps after a row's first block
+ *             [1] of those, steps where the row committed a new max (a rescale)
+ *             [2] 32-row group-block steps after the group's first block
+ *             [3] of those, steps where any row of the group rescaled
+ *             These are the "rows" and "warps" counts of the rescale-frequency
+ *             table on "FlashAttention-4's Softmax Tricks". Counting adds
+ *             atomics, so this entry point is for measurement, not speed.
+ */
+int attn_fwd_stats(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                   int exp2_mode, float tau, int dtype,
+                   const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                   unsigned long long* stats, void* stream);
+
+/*
+ * attn_exp2 -- y[i] = 2^x[i] through the same device exp2 the attention kernels
+ * inline (ATTN_EXP2_HW or ATTN_EXP2_EMU; MIX is not a per-element mode here).
+ *   x, y      device float32 [n]; may alias
+ *   n         >= 0
+ * The software exp2 is defined for x <= 127 and returns 0 for x <= -127 and -inf.
+ */
+int attn_exp2(const float* x, float* y, long n, int exp2_mode, void* stream);
+
+/* Emulated share used by ATTN_EXP2_MIX for (dtype, d, causal), in 16ths; < 0 on
+ * an unsupported combination. */
+int attn_mix_sixteenths(int dtype, int d, int causal);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_H */

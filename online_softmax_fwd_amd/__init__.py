@@ -1,0 +1,173 @@
+"""Python binding of libattn.so, the gfx950 attention forward library.
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels behind the C ABI of ``include/attn.h``. torch is used to allocate
+device memory and to name the stream. There is no CPU path: if libattn.so is
+missing or cannot be loaded, every call raises.
+
+    O, LSE = fwd(q, k, v, causal=False, scale=None, exp2_mode="hw", tau=8.0)
+
+q, k, v: contiguous CUDA (HIP) tensors [B, H, N, d], float32 or bfloat16,
+or uint8 e4m3 bytes with ``q_scale``/``k_scale``/``v_scale`` E8M0 bytes
+[B, H, N/32, d/32] for the MXFP8 path. O has q's dtype (bfloat16 for MXFP8);
+LSE is float32 [B, H, Nq], natural log.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["fwd", "fwd_stats", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
+           "ATTN_F32", "ATTN_BF16", "ATTN_MXFP8_E4M3", "EXP2_MODES", "STATUS"]
+
+ATTN_F32, ATTN_BF16, ATTN_MXFP8_E4M3 = 0, 1, 2
+EXP2_MODES = {"hw": 0, "emu": 1, "mix": 2}
+MIX_BASE = 16
+STATUS = {0: "ATTN_OK", -1: "ATTN_E_NULLPTR", -2: "ATTN_E_SHAPE", -3: "ATTN_E_HEADDIM", -4: "ATTN_E_DTYPE",
+          -5: "ATTN_E_EXP2MODE", -6: "ATTN_E_TAU", -7: "ATTN_E_SCALE", -8: "ATTN_E_ALIGN", -9: "ATTN_E_HIP"}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libattn.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libattn.so (built by online_softmax_fwd_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m online_softmax_fwd_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fwd_args = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, cf]
+    lib.attn_fwd.argtypes = fwd_args
+    lib.attn_fwd.restype = ci
+    lib.attn_fwd_ex.argtypes = fwd_args + [ci, vp, vp, vp, vp]
+    lib.attn_fwd_ex.restype = ci
+    lib.attn_fwd_stats.argtypes = fwd_args + [ci, vp, vp, vp, vp, vp]
+    lib.attn_fwd_stats.restype = ci
+    lib.attn_exp2.argtypes = [vp, vp, ctypes.c_long, ci, vp]
+    lib.attn_exp2.restype = ci
+    lib.attn_mix_sixteenths.argtypes = [ci, ci, ci]
+    lib.attn_mix_sixteenths.restype = ci
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise AttnError(rc, load_library().attn_last_error().decode())
+
+
+def _mode(exp2_mode) -> int:
+    if isinstance(exp2_mode, int):
+        return exp2_mode
+    if exp2_mode.startswith("mix") and exp2_mode[3:].isdigit():   # "mix3" = 3/16 emulated
+        return MIX_BASE + int(exp2_mode[3:])
+    return EXP2_MODES[exp2_mode]
+
+
+def _stream_ptr(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _prepare(q, k, v, out, lse, q_scale, k_scale, v_scale):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d]")
+    if q.dtype == torch.float32:
+        dtype, odt = ATTN_F32, torch.float32
+    elif q.dtype == torch.bfloat16:
+        dtype, odt = ATTN_BF16, torch.bfloat16
+    elif q.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        dtype, odt = ATTN_MXFP8_E4M3, torch.bfloat16
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share a dtype")
+    B, H, Nq, d = q.shape
+    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != d:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != (B, H, Nq, d) or out.dtype != odt or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse has the wrong shape, dtype or layout")
+    scales = [0, 0, 0]
+    if dtype == ATTN_MXFP8_E4M3:
+        for i, (name, s, n) in enumerate((("q_scale", q_scale, Nq), ("k_scale", k_scale, k.shape[2]),
+                                          ("v_scale", v_scale, k.shape[2]))):
+            if s is None or s.dtype != torch.uint8 or not s.is_contiguous() or \
+                    tuple(s.shape) != (B, H, n // 32, d // 32):
+                raise ValueError(f"{name} must be contiguous uint8 [B, H, N/32, d/32]")
+            scales[i] = s.data_ptr()
+    return dtype, out, lse, scales
+
+
+def fwd(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 8.0, out=None, lse=None,
+        q_scale=None, k_scale=None, v_scale=None, stream=None):
+    """Attention forward through attn_fwd_ex. Returns (O, LSE); asynchronous on `stream`."""
+    lib = load_library()
+    dtype, out, lse, scales = _prepare(q, k, v, out, lse, q_scale, k_scale, v_scale)
+    B, H, Nq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           B, H, Nq, k.shape[2], d, int(bool(causal)), scale, _mode(exp2_mode), float(tau),
+                           dtype, scales[0], scales[1], scales[2], _stream_ptr(stream, q.device)))
+    return out, lse
+
+
+def fwd_stats(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 8.0,
+              q_scale=None, k_scale=None, v_scale=None, stream=None):
+    """fwd plus the rescale counters: returns (O, LSE, stats[4] uint64 on the host)."""
+    import torch
+    lib = load_library()
+    dtype, out, lse, scales = _prepare(q, k, v, None, None, q_scale, k_scale, v_scale)
+    B, H, Nq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = torch.zeros(4, dtype=torch.int64, device=q.device)
+    _check(lib.attn_fwd_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              B, H, Nq, k.shape[2], d, int(bool(causal)), scale, _mode(exp2_mode), float(tau),
+                              dtype, scales[0], scales[1], scales[2], st.data_ptr(),
+                              _stream_ptr(stream, q.device)))
+    return out, lse, st.cpu().tolist()
+
+
+def exp2(x, exp2_mode="emu", out=None, stream=None):
+    """The kernels' device exp2 applied to a float32 GPU tensor."""
+    import torch
+    lib = load_library()
+    if not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    y = torch.empty_like(x) if out is None else out
+    _check(lib.attn_exp2(x.data_ptr(), y.data_ptr(), x.numel(), _mode(exp2_mode), _stream_ptr(stream, x.device)))
+    return y
+
+
+def mix_sixteenths(dtype: int, d: int, causal: bool) -> int:
+    return load_library().attn_mix_sixteenths(dtype, d, int(bool(causal)))

@@ -1,0 +1,182 @@
+// attn_api.cpp -- the C ABI declared in include/attn.h: argument validation,
+// the exp2-mix tuning table and dispatch to the per-dtype launchers.
+// Validation runs before any HIP call, so every error path works on a host
+// without a GPU.
+#include "attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "attn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Emulated share of P (16ths) for ATTN_EXP2_MIX, keyed by (dtype, d, causal).
+// Starting points are the shares the first page reports for the Blackwell
+// kernel's tuning table ("FlashAttention-4's Softmax Tricks", section "The
+// emulated exp2": 18.75 % non-causal d=128, 12.5 % causal d=128, 25 % FP8);
+// measured gfx950 values replace them where the bench has been run.
+int mix_table(int dtype, int d, int causal) {
+  if (d != 64 && d != 128) return -1;
+  switch (dtype) {
+    case ATTN_BF16:
+      if (d == 128) return causal ? 2 : 3;
+      return 4;
+    case ATTN_F32:
+      return 2;
+    case ATTN_MXFP8_E4M3:
+      return 4;
+    default:
+      return -1;
+  }
+}
+
+int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                      int B, int H, int Nq, int Nk, int d, int causal, float scale, int exp2_mode, float tau,
+                      int dtype, const uint8_t* qs, const uint8_t* ks, const uint8_t* vs, bool* nothing) {
+  *nothing = false;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_MXFP8_E4M3)
+    return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32, ATTN_BF16 or ATTN_MXFP8_E4M3", dtype);
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(ATTN_E_SHAPE, "negative size (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
+  if (d != 64 && d != 128) return fail(ATTN_E_HEADDIM, "head dim d=%d is not 64 or 128", d);
+  if (causal != 0 && causal != 1) return fail(ATTN_E_SHAPE, "causal=%d is not 0 or 1", causal);
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(ATTN_E_SCALE, "scale=%g must be finite and > 0 (the row max is kept in raw score units)",
+                (double)scale);
+  if (!std::isfinite(tau) || tau < 0.0f || tau > 64.0f)
+    return fail(ATTN_E_TAU, "tau=%g must be finite and in [0, 64]", (double)tau);
+  int emu16;
+  if (exp2_mode == ATTN_EXP2_HW) {
+    emu16 = 0;
+  } else if (exp2_mode == ATTN_EXP2_EMU) {
+    emu16 = 16;
+  } else if (exp2_mode == ATTN_EXP2_MIX) {
+    emu16 = mix_table(dtype, d, causal);
+  } else if (exp2_mode >= ATTN_EXP2_MIX_BASE && exp2_mode <= ATTN_EXP2_MIX_BASE + 16) {
+    emu16 = exp2_mode - ATTN_EXP2_MIX_BASE;
+  } else {
+    return fail(ATTN_E_EXP2MODE, "exp2_mode=%d is not HW (0), EMU (1), MIX (2) or MIX_BASE+k (16..32)",
+                exp2_mode);
+  }
+  if (emu16 < 0 || !attn::emu16_supported(emu16))
+    return fail(ATTN_E_EXP2MODE, "no kernel instance emulates %d/16 of the exponentials", emu16);
+
+  const long long rows = (long long)B * H * Nq;
+  if (rows == 0) {
+    *nothing = true;
+    return ATTN_OK;
+  }
+  if (Nk < 1) return fail(ATTN_E_SHAPE, "Nk=%d: softmax over an empty key set is undefined", Nk);
+  const long long n_qt = (Nq + 127) / 128;
+  if ((long long)B * H * n_qt > 0x7FFFFFFFLL || Nq > (1 << 30) || Nk > (1 << 30))
+    return fail(ATTN_E_SHAPE, "sizes too large (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
+  if (dtype == ATTN_MXFP8_E4M3 && (Nq % 32 != 0 || Nk % 32 != 0))
+    return fail(ATTN_E_SHAPE, "MXFP8 needs Nq and Nk to be multiples of 32 (Nq=%d Nk=%d)", Nq, Nk);
+  if (!Q || !K || !V || !O || !LSE) return fail(ATTN_E_NULLPTR, "Q, K, V, O and LSE must be non-NULL");
+  if (dtype == ATTN_MXFP8_E4M3 && (!qs || !ks || !vs))
+    return fail(ATTN_E_NULLPTR, "MXFP8 needs q_scale, k_scale and v_scale");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return fail(ATTN_E_ALIGN, "Q, K, V, O and LSE must be 16-byte aligned");
+
+  a.q = Q;
+  a.k = K;
+  a.v = V;
+  a.o = O;
+  a.lse = LSE;
+  a.q_scale = qs;
+  a.k_scale = ks;
+  a.v_scale = vs;
+  a.stats = nullptr;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.causal = causal;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
+  a.tau = tau;
+  a.emu16 = emu16;
+  return ATTN_OK;
+}
+
+int run(const attn::FwdArgs& a, int dtype, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (dtype) {
+    case ATTN_BF16: e = attn::launch_fwd_bf16(a, s); break;
+    case ATTN_F32: e = attn::launch_fwd_f32(a, s); break;
+    default: e = attn::launch_fwd_mxfp8(a, s); break;
+  }
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int Nq, int Nk,
+                int d, int causal, float scale, int exp2_mode, float tau, int dtype, const uint8_t* q_scale,
+                const uint8_t* k_scale, const uint8_t* v_scale, void* stream) {
+  attn::FwdArgs a;
+  bool nothing;
+  int rc = validate_and_fill(a, Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, exp2_mode, tau, dtype, q_scale,
+                             k_scale, v_scale, &nothing);
+  if (rc != ATTN_OK || nothing) return rc;
+  return run(a, dtype, stream);
+}
+
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int Nq, int Nk, int d,
+             int causal, float scale, int exp2_mode, float tau) {
+  return attn_fwd_ex(Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, exp2_mode, tau, ATTN_BF16, nullptr, nullptr,
+                     nullptr, nullptr);
+}
+
+int attn_fwd_stats(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int Nq, int Nk,
+                   int d, int causal, float scale, int exp2_mode, float tau, int dtype, const uint8_t* q_scale,
+                   const uint8_t* k_scale, const uint8_t* v_scale, unsigned long long* stats, void* stream) {
+  attn::FwdArgs a;
+  bool nothing;
+  int rc = validate_and_fill(a, Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, exp2_mode, tau, dtype, q_scale,
+                             k_scale, v_scale, &nothing);
+  if (rc != ATTN_OK) return rc;
+  if (!stats) return fail(ATTN_E_NULLPTR, "stats must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(stats) & 7u) != 0) return fail(ATTN_E_ALIGN, "stats must be 8-byte aligned");
+  if (nothing) return ATTN_OK;
+  a.stats = stats;
+  return run(a, dtype, stream);
+}
+
+int attn_exp2(const float* x, float* y, long n, int exp2_mode, void* stream) {
+  if (exp2_mode != ATTN_EXP2_HW && exp2_mode != ATTN_EXP2_EMU)
+    return fail(ATTN_E_EXP2MODE, "attn_exp2 takes ATTN_EXP2_HW (0) or ATTN_EXP2_EMU (1), got %d", exp2_mode);
+  if (n < 0) return fail(ATTN_E_SHAPE, "n=%ld is negative", n);
+  if (n == 0) return ATTN_OK;
+  if (!x || !y) return fail(ATTN_E_NULLPTR, "x and y must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(y) & 3u))
+    return fail(ATTN_E_ALIGN, "x and y must be 4-byte aligned");
+  hipError_t e = attn::launch_exp2(x, y, n, exp2_mode == ATTN_EXP2_EMU, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+int attn_mix_sixteenths(int dtype, int d, int causal) { return mix_table(dtype, d, causal ? 1 : 0); }
+
+const char* attn_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// attn_internal.h -- host-side interface between the C ABI (attn_api.cpp) and
+// the kernel launchers (one .hip file per input dtype). Not installed.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Arguments after validation. Pointers are device pointers.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const uint8_t* q_scale;   // MXFP8 only
+  const uint8_t* k_scale;
+  const uint8_t* v_scale;
+  unsigned long long* stats;  // optional rescale counters (4 x uint64)
+  int B, H, Nq, Nk, d;
+  int causal;
+  float scale_log2;         // scale * log2(e)
+  float tau;                // lagging-max threshold, log2 units
+  int emu16;                // software-exp2 share of P, in 16ths (0 = all hardware)
+};
+
+// Each returns hipSuccess or the launch error; none synchronises.
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_mxfp8(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_exp2(const float* x, float* y, long n, int emulated, hipStream_t stream);
+
+// Emulated shares (in 16ths) that have a compiled kernel instance.
+bool emu16_supported(int emu16);
+
+}  // namespace attn

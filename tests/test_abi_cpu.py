@@ -1,0 +1,121 @@
+"""The C ABI on a host without a GPU: the library loads, exports every symbol
+include/attn.h declares, and rejects bad arguments before any HIP call.
+
+No call here reaches a kernel launch: every call is either invalid (the
+validation returns first) or has nothing to do (B*H*Nq == 0)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from online_softmax_fwd_amd import build, load_library
+    if not os.path.exists(build.LIB_PATH):
+        build.build_library(verbose=False)
+    return load_library()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert names == sorted(["attn_exp2", "attn_fwd", "attn_fwd_ex", "attn_fwd_stats", "attn_last_error",
+                            "attn_mix_sixteenths"])
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {lib._name}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+FAKE = 0x10000            # 16-byte aligned, never dereferenced: validation fails first
+GOOD = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, B=1, H=1, Nq=128, Nk=128, d=128, causal=0,
+            scale=0.088, mode=0, tau=8.0, dtype=1, qs=None, ks=None, vs=None)
+
+
+def _call(lib, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return lib.attn_fwd_ex(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                           a["causal"], a["scale"], a["mode"], a["tau"], a["dtype"], a["qs"], a["ks"], a["vs"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), -4),
+    (dict(B=-1), -2),
+    (dict(Nk=0), -2),
+    (dict(d=96), -3),
+    (dict(d=256), -3),
+    (dict(causal=2), -2),
+    (dict(scale=0.0), -7),
+    (dict(scale=-1.0), -7),
+    (dict(scale=float("nan")), -7),
+    (dict(scale=float("inf")), -7),
+    (dict(tau=-1.0), -6),
+    (dict(tau=float("nan")), -6),
+    (dict(tau=65.0), -6),
+    (dict(mode=3), -5),
+    (dict(mode=16 + 5), -5),          # no instance emulates 5/16
+    (dict(mode=16 + 17), -5),
+    (dict(Q=None), -1),
+    (dict(LSE=None), -1),
+    (dict(O=FAKE + 4), -8),
+    (dict(dtype=2, Nq=100), -2),      # MXFP8 needs multiples of 32
+    (dict(dtype=2), -1),              # MXFP8 needs scales
+    (dict(Nq=1 << 31 - 1, B=1 << 20), -2),
+])
+def test_validation_errors(lib, kw, code):
+    assert _call(lib, **kw) == code
+    assert lib.attn_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Nq=0), dict(Nq=0, Nk=0)])
+def test_nothing_to_do_is_ok_without_touching_memory(lib, kw):
+    assert _call(lib, Q=None, K=None, V=None, O=None, LSE=None, **kw) == 0
+
+
+def test_attn_fwd_is_bf16_on_the_null_stream(lib):
+    assert lib.attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 16, 100, 0, 0.1, 0, 8.0) == -3
+    assert lib.attn_fwd(None, None, None, None, None, 0, 1, 16, 16, 64, 0, 0.1, 0, 8.0) == 0
+
+
+def test_exp2_validation(lib):
+    assert lib.attn_exp2(FAKE, FAKE, 10, 2, None) == -5
+    assert lib.attn_exp2(FAKE, FAKE, -1, 0, None) == -2
+    assert lib.attn_exp2(None, None, 0, 1, None) == 0
+    assert lib.attn_exp2(None, FAKE, 5, 1, None) == -1
+    assert lib.attn_exp2(FAKE + 2, FAKE, 5, 1, None) == -8
+
+
+def test_stats_validation(lib):
+    a = GOOD
+    args = [a["Q"], a["K"], a["V"], a["O"], a["LSE"], 1, 1, 128, 128, 128, 0, 0.1, 0, 8.0, 1, None, None, None]
+    assert lib.attn_fwd_stats(*args, None, None) == -1
+    assert lib.attn_fwd_stats(*args, FAKE + 4, None) == -8
+
+
+def test_mix_table(lib):
+    for dtype in (0, 1, 2):
+        for d in (64, 128):
+            for causal in (0, 1):
+                k = lib.attn_mix_sixteenths(dtype, d, causal)
+                assert 0 <= k <= 16
+    assert lib.attn_mix_sixteenths(1, 96, 0) < 0
+    assert lib.attn_mix_sixteenths(9, 128, 0) < 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    import online_softmax_fwd_amd as attn
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        attn.fwd(x, x, x)
