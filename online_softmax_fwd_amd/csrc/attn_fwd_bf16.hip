@@ -1,8 +1,8 @@
 // attn_fwd_bf16.hip -- bf16 attention forward for gfx950 (MI355X).
 //
-// A workgroup of NW waves owns 32*NW query rows of one (batch, head); each
-// wave owns 32 rows. K and V stream through LDS in BN-key tiles, two stages
-// deep; per row the wave keeps a running max m (raw score units), a
+// A workgroup of 8 waves owns 256 query rows of one (batch, head); each wave
+// owns 32 rows. K and V stream through LDS in 64-key tiles, two buffers per
+// tensor; per row the wave keeps a running max m (raw score units), a
 // denominator l and a 32 x d float accumulator, so S and P never reach
 // memory. Per tile and wave:
 //
@@ -14,8 +14,8 @@
 //   mask                  only on tiles that cross the causal diagonal or the
 //                         end of the keys ("Lecture 2 -- Online Softmax and
 //                         Numerical Correctness", section "Causal masking just
-//                         changes which blocks contribute"); tiles wholly above
-//                         the diagonal are never loaded.
+//                         changes which blocks contribute"); tiles above the
+//                         workgroup's diagonal are never loaded.
 //   lagging max           "FlashAttention-4's Softmax Tricks", section
 //                         "Conditional rescaling, and when it's exact": keep the
 //                         stale max while (m_old - m_new) * scale_log2 >= -tau,
@@ -24,7 +24,7 @@
 //   P = 2^(S*c - m*c)     one FMA then exp2 (the exp2 fold of "Flash Attention 4
 //                         -- the algorithm and the two-MMA problem", section "The
 //                         exp2 trick"): hardware, software, or a fixed mix
-//   l = alpha*l + sum P   from the float32 P, an in-lane partial per half
+//   l = alpha*l + sum P   from the float32 P
 //   O^T += V^T P^T        v_mfma_f32_32x32x16_bf16; A = V^T read from the
 //                         row-major V tile with ds_read_b64_tr_b16, B = P in
 //                         bf16 taken straight from the S^T registers (the K rows
@@ -42,6 +42,10 @@
 //   - the K reads of one instruction (32 rows x one chunk) and
 //   - the V transpose reads (8 rows x 4 chunks)
 // each spread evenly over the 64 LDS banks.
+//
+// Schedule: see "Ping-pong schedule" below.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -85,83 +89,191 @@ __device__ __forceinline__ int key_of_row(int m) {
   return ((g >> 1) << 4) | (h << 3) | ((g & 1) << 2) | r;
 }
 
-template <class C, bool CAUSAL, int EMU16>
-struct Body {
-  // per-lane constants
-  int lane, wave, hh, l32;
-  int qi, qw0;
-  uint32_t koff[C::D / 16];   // K operand read offsets, one per 16-wide d step
-  uint32_t voff[C::D / 32];   // V transpose read offsets, one per 32-wide d block
-  uint32_t kld[C::LOADS];     // global byte offsets of this lane's K chunks within a tile
-  uint32_t vld[C::LOADS];
-  __amdgpu_buffer_rsrc_t rk, rv;
-
-  __device__ __forceinline__ void issue_loads(int t, char* ks, char* vs) {
-    const uint32_t soff = (uint32_t)t * C::TILE;
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int j = wave + C::NW * i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(ks + 1024 * j), 16, kld[i], soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vs + 1024 * j), 16, vld[i], soff, 0, 0);
-    }
-  }
-};
-
 __device__ __forceinline__ void wait_own_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int D, int BN, int NW, bool CAUSAL, int EMU16>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
+// One wave-wide 16-byte-per-lane DMA from a buffer into LDS: lane i's 16 bytes
+// at byte voff + soff of the buffer land at lds + 16 * i. (Kept in a device
+// function: the host compilation pass must not see this builtin in a kernel
+// body.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Cross-half reductions with v_permlane32_swap: it exchanges the upper half of
+// one register with the lower half of the other, so (r[0], r[1]) is
+// (x[l], x[l ^ 32]) in some order in every lane, and max/sum of the pair is
+// the pair's reduction (the sum is formed lower half + upper half in both).
+__device__ __forceinline__ float pl_max_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float pl_sum_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+
+// Sum and max of a wave's 32 per-lane scores as balanced trees (depth 5 and
+// 4) instead of serial chains, so the softmax stage is not latency-bound.
+template <int KB>
+__device__ __forceinline__ float tree_sum(const floatx16 (&x)[KB]) {
+  float t[8 * KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[8 * kb + e] = x[kb][e] + x[kb][e + 8];
+#pragma unroll
+  for (int w = 4 * KB; w >= 1; w >>= 1)
+#pragma unroll
+    for (int e = 0; e < w; ++e) t[e] = t[e] + t[e + w];
+  return t[0];
+}
+template <int KB>
+__device__ __forceinline__ float tree_max(const floatx16 (&x)[KB]) {
+  float t[8 * KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[8 * kb + e] = __builtin_fmaxf(x[kb][e], x[kb][e + 8]);
+#pragma unroll
+  for (int w = 4 * KB; w >= 1; w >>= 1)
+#pragma unroll
+    for (int e = 0; e < w; ++e) t[e] = __builtin_fmaxf(t[e], t[e + w]);
+  return t[0];
+}
+
+// ---------------------------------------------------------------------------
+// The MFMA phase as one software-pipelined sequence: the PV MFMAs of the
+// previous tile, then the S^T MFMAs of the current tile. Operands come from
+// LDS through a ring RING MFMAs deep (the LDS round trip is several MFMA
+// durations long), and consecutive MFMAs rotate over independent accumulators
+// (the 4 (d=128) or 2 (d=64) blocks of O^T, then the 2 blocks of S^T).
+// While the first operands are in flight the wave converts the previous
+// tile's float32 P (left in s by the softmax stage) to bf16 and folds its row
+// sum into l, so that VALU work rides in the MFMA stage's idle issue slots.
+// sched_barrier pins the issue order so the reads stay ahead.
+// ---------------------------------------------------------------------------
+template <int D, int KB, int RB, bool DO_PV, bool DO_QK>
+__device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&s)[KB], float& l_run, float alpha,
+                                              const bf16x8 (&qf)[D / 16], const char* ksrc, const char* vsrc,
+                                              const uint32_t (&koff)[D / 16], const uint32_t (&voff)[D / 32]) {
+  constexpr int NDB = D / 32;
+  constexpr int NPV = DO_PV ? NDB * KB * 2 : 0;
+  constexpr int NQK = DO_QK ? KB * (D / 16) : 0;
+  constexpr int N = NPV + NQK;
+  constexpr int RING = 6;
+  auto read = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+    if (i < NPV) {
+      const int db = i % NDB, k = i / NDB, kb = k >> 1, cc = k & 1;
+      const char* vp = vsrc + voff[db] + (kb * 32 + 16 * cc) * RB;
+      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp));
+      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp + 4 * RB));
+      return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                              __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+    }
+    const int q = i - NPV, kb = q % KB, st = q / KB;
+    return *(const bf16x8*)(ksrc + kb * 32 * RB + koff[st]);
+  };
+  bf16x8 ring[RING];
+#pragma unroll
+  for (int i = 0; i < RING && i < N; ++i) ring[i] = read(i);
+
+  bf16x8 pb[KB][2];
+  if constexpr (DO_PV) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[kb][cc][e] = (__bf16)s[kb][8 * cc + e];
+    l_run = __builtin_fmaf(l_run, alpha, tree_sum<KB>(s));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto mma = [&](int i, const bf16x8& a) __attribute__((always_inline)) {
+    if (i < NPV) {
+      const int db = i % NDB, k = i / NDB, kb = k >> 1, cc = k & 1;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][cc], o[db], 0, 0, 0);
+    } else {
+      const int q = i - NPV, kb = q % KB, st = q / KB;
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? floatx16{} : s[kb], 0, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bf16x8 a = ring[i % RING];
+    if (i + RING < N) ring[i % RING] = read(i + RING);
+    mma(i, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong schedule. The 8 waves form two groups of 4 (one wave of each
+// group per SIMD). Each wave runs, per K/V tile j,
+//     MFMA phase M(j): O^T += V_{j-1}^T P_{j-1}^T   and   S_j^T = K_j Q^T
+//     VALU phase V(j): mask, row max, lagging-max rescale, P_j = exp2, row sum
+// and group 1 runs one phase behind group 0, with a workgroup barrier between
+// phases: while one wave of a SIMD issues MFMAs the other issues the softmax
+// VALU work, so the matrix core and the vector ALU overlap. Tile j's K and
+// V_{j-1} are read in the two half-phases 2j and 2j+1; the DMA for K_{j+1} and
+// V_j is issued at the start of half-phase 2j into the other buffer of each
+// pair and waited for at the end of half-phase 2j+1.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, int EMU16>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                      __bf16* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats,
                      int H, int Nq, int Nk, int n_qt, float c, float tau) {
-  using C = Cfg<D, BN, NW>;
-  __shared__ __attribute__((aligned(1024))) char k0s[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char v0s[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char k1s[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char v1s[C::TILE];
+  using C = Cfg<D, 64, 8>;
+  constexpr int BN = C::BN, KB = C::KB;
+  __shared__ __attribute__((aligned(1024))) char kb0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[C::TILE];
 
-  Body<C, CAUSAL, EMU16> bd;
   const int tid = threadIdx.x;
-  bd.lane = tid & 63;
-  bd.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  bd.hh = bd.lane >> 5;
-  bd.l32 = bd.lane & 31;
-  const int lane = bd.lane, hh = bd.hh, l32 = bd.l32;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int hh = lane >> 5, l32 = lane & 31;
 
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
   const int bh = logical / n_qt;
   int qt = logical - bh * n_qt;
   if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
   const int q0 = qt * C::BM;
-  const int qw0 = q0 + bd.wave * 32;
+  const int qw0 = q0 + wave * 32;
   const int qi = qw0 + l32;
   const size_t qbase = (size_t)bh * Nq * D;
   const size_t kbase = (size_t)bh * Nk * D;
 
   // ---- per-lane constants --------------------------------------------------
+  uint32_t koff[D / 16], voff[D / 32], kld[C::LOADS], vld[C::LOADS];
   {
     const int krow = key_of_row(l32);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      bd.koff[s] = krow * C::RB + 16 * ((2 * s + hh) ^ swz_k<D>(krow));
+    for (int s = 0; s < D / 16; ++s) koff[s] = krow * C::RB + 16 * ((2 * s + hh) ^ swz_k<D>(krow));
     const int L = lane & 15, gidx = (lane >> 4) & 1;
     const int vr = 8 * hh + (L >> 2);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int cch = 4 * db + 2 * gidx + ((L & 3) >> 1);
-      bd.voff[db] = vr * C::RB + 16 * (cch ^ swz_v<D>(vr)) + 8 * (L & 1);
+      voff[db] = vr * C::RB + 16 * (cch ^ swz_v<D>(vr)) + 8 * (L & 1);
     }
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int pos = 64 * (bd.wave + NW * i) + lane;
+      const int pos = 64 * (wave + 8 * i) + lane;
       const int r = pos / C::CH, p = pos % C::CH;
-      bd.kld[i] = r * C::RB + 16 * (p ^ swz_k<D>(r));
-      bd.vld[i] = r * C::RB + 16 * (p ^ swz_v<D>(r));
+      kld[i] = r * C::RB + 16 * (p ^ swz_k<D>(r));
+      vld[i] = r * C::RB + 16 * (p ^ swz_v<D>(r));
     }
-    const int nrec = Nk * C::RB;
-    bd.rk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + kbase), (short)0, nrec, 0x00020000);
-    bd.rv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + kbase), (short)0, nrec, 0x00020000);
   }
+  const int nrec = Nk * C::RB;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + kbase), (short)0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + kbase), (short)0, nrec, 0x00020000);
 
   // ---- Q as the B operand: lane (h, n) holds Q[n][16s + 8h .. +8] -----------
   bf16x8 qf[D / 16];
@@ -176,53 +288,54 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 
   const int kend = CAUSAL ? min(Nk, q0 + C::BM) : Nk;
-  const int n_kt = (kend + BN - 1) / BN;
+  const int T = (kend + BN - 1) / BN;
 
   floatx16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = floatx16{};
+  floatx16 s[KB];        // S^T of the current tile, then its float32 P
+  float alpha_p = 1.0f;  // rescale factor of the tile whose P is in s
   float m_run = kNegInf;  // running max, raw score units
   float l_run = 0.0f;     // running denominator over this lane's half of the keys
   unsigned long long cnt[4] = {0, 0, 0, 0};
 
-  auto compute = [&](int t, const char* ks, const char* vs) {
-    const int k0 = t * BN;
-    if (CAUSAL && k0 > qw0 + 31) return;  // wave-uniform: every key of the tile is masked
-
-    // S^T = K Q^T
-    floatx16 s[C::KB];
+  // DMA of this wave's share of K_{j+1} (into kdst) and V_j (into vdst)
+  auto load_tiles = [&](int j, char* kdst, char* vdst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      s[kb] = floatx16{};
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 a = *(const bf16x8*)(ks + kb * 32 * C::RB + bd.koff[st]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int slot = 1024 * (wave + 8 * i);
+      if (j + 1 < T)
+        dma16(rk, kdst + slot, kld[i], (uint32_t)(j + 1) * C::TILE);
+      if (j < T)
+        dma16(rv, vdst + slot, vld[i], (uint32_t)j * C::TILE);
     }
+  };
 
+  // MFMA phase: PV of tile j-1 from vsrc (DO_PV) and S^T of tile j from ksrc (DO_QK)
+  auto mfma_phase = [&](auto do_pv, auto do_qk, const char* ksrc, const char* vsrc) __attribute__((always_inline)) {
+    mfma_sequence<D, KB, C::RB, decltype(do_pv)::value, decltype(do_qk)::value>(o, s, l_run, alpha_p, qf, ksrc, vsrc,
+                                                                                  koff, voff);
+  };
+
+  // VALU phase j: softmax of tile j
+  auto valu_phase = [&](int j) __attribute__((always_inline)) {
+    const int k0 = j * BN;
     if ((CAUSAL && k0 + BN - 1 > qw0) || (k0 + BN > Nk)) {
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = k0 + kb * 32 + 16 * (j >> 3) + 8 * hh + (j & 7);
-          if (key >= Nk || (CAUSAL && key > qi)) s[kb][j] = kNegInf;
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + kb * 32 + 16 * (e >> 3) + 8 * hh + (e & 7);
+          if (key >= Nk || (CAUSAL && key > qi)) s[kb][e] = kNegInf;
         }
     }
-
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, s[kb][j]);
-    mx = max_halves(mx);
+    const float mx = pl_max_halves(tree_max<KB>(s));
 
     const float m_new = __builtin_fmaxf(m_run, mx);
     const float acc = (m_run - m_new) * c;  // -inf on a row's first block
     const bool seen = mx > kNegInf;
     const bool commit = seen && !(acc >= -tau);
-    const float alpha = commit ? exp2_hw(acc) : 1.0f;
+    alpha_p = commit ? exp2_hw(acc) : 1.0f;
     if (stats) {
       const bool step = seen && (m_run > kNegInf) && hh == 0 && qi < Nq;
       const unsigned long long bs = __builtin_amdgcn_ballot_w64(step);
@@ -235,63 +348,69 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     m_run = commit ? m_new : m_run;
     if (__builtin_amdgcn_ballot_w64(commit)) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha_p;
     }
-
+    // P = 2^(S*c - m*c), left in s as float32; the MFMA stage converts it to
+    // bf16 and adds its row sum to l (after l *= alpha_p)
     const float mc = (m_run > kNegInf) ? m_run * c : 0.0f;
-    float rs = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = exp2_sel<EMU16>(__builtin_fmaf(s[kb][j], c, -mc), j);
-        s[kb][j] = p;
-        rs += p;
-      }
-    l_run = l_run * alpha + rs;
-
-    bf16x8 pb[C::KB][2];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[kb][cc][e] = (__bf16)s[kb][8 * cc + e];
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const char* vp = vs + bd.voff[db] + (kb * 32 + 16 * cc) * C::RB;
-          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp));
-          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp + 4 * C::RB));
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][cc], o[db], 0, 0, 0);
-        }
+      for (int e = 0; e < 16; ++e) s[kb][e] = exp2_sel<EMU16>(__builtin_fmaf(s[kb][e], c, -mc), e);
   };
 
-  bd.issue_loads(0, k0s, v0s);
+  // One step j = [MFMA phase j] barrier [VALU phase j] barrier, identical for
+  // both groups; group 1 runs it one barrier later. Every DMA is issued at
+  // half-phase 2j (group 0 at the start of its MFMA phase j, group 1 at the
+  // start of its VALU phase j-1) and waited for at the end of half-phase 2j+1.
+  // The caller passes the LDS arrays for the parity of j, so every LDS access
+  // has a known target. Step 0 has no PV and step T no S^T or softmax; every
+  // other step runs the full MFMA phase for every wave, also on tiles that the
+  // causal mask empties for some of its rows (the softmax turns those into
+  // P = 0), which keeps the loop free of data-dependent branches.
+  auto step = [&](int j, auto do_pv, auto do_qk, char* kcur, char* knxt, char* vprv, char* vcur)
+      __attribute__((always_inline)) {
+    if (group == 0) load_tiles(j, knxt, vcur);
+    mfma_phase(do_pv, do_qk, kcur, vprv);
+    if (group == 1) wait_own_loads();
+    __syncthreads();
+    if (group == 1) load_tiles(j + 1, kcur, vprv);
+    if constexpr (decltype(do_qk)::value) valu_phase(j);
+    if (group == 0) wait_own_loads();
+    __syncthreads();
+  };
+  using Y = std::true_type;
+  using N = std::false_type;
+
+  // prologue: K_0 by every wave
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) dma16(rk, kb0 + 1024 * (wave + 8 * i), kld[i], 0);
   wait_own_loads();
   __syncthreads();
-  for (int t = 0; t < n_kt; t += 2) {
-    if (t + 1 < n_kt) bd.issue_loads(t + 1, k1s, v1s);
-    compute(t, k0s, v0s);
-    wait_own_loads();
-    __syncthreads();
-    if (t + 1 >= n_kt) break;
-    if (t + 2 < n_kt) bd.issue_loads(t + 2, k0s, v0s);
-    compute(t + 1, k1s, v1s);
-    wait_own_loads();
+  if (group == 1) {
+    // group 1's share of K_1 and V_0 goes out with group 0's, at half-phase 0
+    load_tiles(0, kb1, vb0);
     __syncthreads();
   }
+  step(0, N{}, Y{}, kb0, kb1, vb1, vb0);
+  int j = 1;
+  for (; j + 1 < T; j += 2) {
+    step(j, Y{}, Y{}, kb1, kb0, vb0, vb1);
+    step(j + 1, Y{}, Y{}, kb0, kb1, vb1, vb0);
+  }
+  if (j < T) {
+    step(j, Y{}, Y{}, kb1, kb0, vb0, vb1);
+    ++j;
+  }
+  // j == T: PV of the last tile
+  if (j & 1)
+    step(j, Y{}, N{}, kb1, kb0, vb0, vb1);
+  else
+    step(j, Y{}, N{}, kb0, kb1, vb1, vb0);
+  if (group == 0) __syncthreads();
 
   // ---- epilogue: O / l, LSE -------------------------------------------------
-  const float l_tot = sum_halves(l_run);
+  const float l_tot = pl_sum_halves(l_run);
   const float inv = 1.0f / l_tot;
   if (qi < Nq) {
     __bf16* op = O + qbase + (size_t)qi * D + 4 * hh;
@@ -312,18 +431,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 }
 
-// Tile shape per head dim: waves per workgroup and keys per tile.
-template <int D> struct Shape;
-template <> struct Shape<128> { static constexpr int NW = 4, BN = 64; };
-template <> struct Shape<64> { static constexpr int NW = 4, BN = 64; };
-
 template <int D, bool CAUSAL, int EMU16>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NW = Shape<D>::NW, BN = Shape<D>::BN;
-  constexpr int BM = 32 * NW;
+  constexpr int BM = Cfg<D, 64, 8>::BM;
   const int n_qt = (a.Nq + BM - 1) / BM;
   const long long grid = (long long)a.B * a.H * n_qt;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, CAUSAL, EMU16>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EMU16>), dim3((unsigned)grid), dim3(512), 0, stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.stats, a.H,
                      a.Nq, a.Nk, n_qt, a.scale_log2, a.tau);
   return hipGetLastError();
