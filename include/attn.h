@@ -52,7 +52,8 @@ enum {
   ATTN_E_EXP2MODE = -5,  /* unknown exp2_mode                                          */
   ATTN_E_TAU = -6,       /* tau negative, above 64 or not finite                       */
   ATTN_E_SCALE = -7,     /* scale not finite or <= 0                                   */
-  ATTN_E_ALIGN = -8,     /* a tensor pointer is not 16-byte aligned                    */
+  ATTN_E_ALIGN = -8,     /* a tensor pointer is not 16-byte aligned (MX scale pointers:
+                            4-byte aligned)                                            */
   ATTN_E_HIP = -9        /* a HIP launch failed (message has the HIP error string)     */
 };
 

@@ -1,9 +1,388 @@
-// attn_fwd_mxfp8.hip -- block-scaled e4m3 attention forward for gfx950.
+// attn_fwd_mxfp8.hip -- block-scaled e4m3 (MXFP8) attention forward for gfx950.
+//
+// Inputs: Q, K, V as OCP e4m3 bytes [B,H,N,128] with one E8M0 byte per 32x32
+// block ([B,H,N/32,4]; V blocked along the sequence with the same square
+// blocks) -- "PyTorch FlashAttention-4 adds MXFP8 block-scaled forward and
+// backward for Blackwell", section "Quantization along both axes and jagged
+// tensors". Output O is bf16, LSE float32.
+//
+// Both contractions run on v_mfma_scale_f32_32x32x64_f8f6f4, which takes the
+// E8M0 scales per lane and applies them inside the MFMA. Its operand layout
+// (measured on the GPU): lane l holds 32 bytes of row l % 32; bytes 0..15 of
+// lanes m and m+32 form K-block 0 (scaled by lane m's scale byte) and bytes
+// 16..31 form K-block 1 (scaled by lane m+32's byte). So every MFMA consumes
+// two 32-wide MX blocks, one scale per lane, selected from a packed scale
+// dword by op_sel.
+//
+// Workgroup: 4 waves x 32 query rows; K and V stream through LDS in 64-key
+// tiles (two buffers each, filled by buffer_load_dwordx4 ... lds). Per tile:
+//   S^T = K Q^T        2 key blocks x 2 MFMAs (d = 128 = 2 x 64)
+//   softmax            mask, block maxima of the two 32-key blocks (in-lane
+//                      tree + v_permlane32_swap), lagging max ("FlashAttention-4's
+//                      Softmax Tricks", "Conditional rescaling"), P = exp2 (hw,
+//                      software or mix), l from float32 P
+//   P -> e4m3          per 32-key block, as the MXFP8 page's "Softmax conversion
+//                      and unroll-KV" section describes: the block amax comes
+//                      from the softmax block max already computed (exp is
+//                      monotone: amax = 2^((blockmax - m) * c), one exp per 32
+//                      keys), the E8M0 byte from the float32 exponent and
+//                      mantissa bits of amax (smallest power of two X with
+//                      amax / X <= 448), then P / X is converted with
+//                      v_cvt_pk_fp8_f32.
+//   O^T += V^T P^T     4 MFMAs (d blocks), A = V^T via ds_read_b64_tr_b8, B = P
+//                      bytes straight from the S^T registers: the K rows
+//                      feeding S^T are permuted so lane half h holds keys
+//                      16h..16h+15 of each 32-key block, i.e. one half of an MX
+//                      block, exactly the PV operand layout.
+// Epilogue: O / l (deferred normalisation) and LSE = ln2 * (m*c + log2 l).
 #include "attn_device.h"
 #include "attn_internal.h"
 
 namespace attn {
+namespace {
 
-hipError_t launch_fwd_mxfp8(const FwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+typedef int intx2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) intx2 lds_intx2;
+
+constexpr int kD = 128;
+constexpr int kRB = kD;                        // bytes per K/V row (one byte per element)
+constexpr int kCH = kRB / 16;                  // 16-byte chunks per row
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;               // query rows per workgroup
+constexpr int kBN = 64;                        // keys per tile
+constexpr int kTile = kBN * kRB;               // bytes per K or V tile
+constexpr int kLoads = kBN * kCH / 64 / kWaves;  // wave-loads per wave per tensor per tile
+static_assert(kLoads * 64 * kWaves == kBN * kCH, "tile split");
+
+// S^T A-operand row m reads key key_of_row(m) of its 32-key block: the 32x32
+// output then holds keys 16h + e (e = 0..15) in lane half h.
+__device__ __forceinline__ int key_of_row(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+// Swizzles of the 16-byte chunks (position c ^ f(r)). The K reads of one
+// instruction take one chunk from 16 rows (the permuted key rows above) per
+// 16-lane group; the V transpose reads take 2 chunks from 16 rows. Rows are
+// 128 bytes, so a 256-byte bank line holds two rows.
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ ((r >> 4) << 2)) & 7; }
+__device__ __forceinline__ int swz_v(int r) { return ((r >> 1) & 3) << 1; }
+
+__device__ __forceinline__ void wait_own_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ float pl_max_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float pl_sum_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ float max16(const floatx16& x) {
+  float t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = __builtin_fmaxf(x[e], x[e + 8]);
+#pragma unroll
+  for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+    for (int e = 0; e < w; ++e) t[e] = __builtin_fmaxf(t[e], t[e + w]);
+  return t[0];
+}
+__device__ __forceinline__ float sum16(const floatx16& x) {
+  float t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = x[e] + x[e + 8];
+#pragma unroll
+  for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+    for (int e = 0; e < w; ++e) t[e] = t[e] + t[e + w];
+  return t[0];
+}
+
+// E8M0 byte of the smallest power of two X with amax / X <= 448 (e4m3's
+// largest finite value), read off the float32 bits of amax >= 0: with
+// amax = 1.f * 2^e, X = 2^(e-8) when 1.f <= 1.75, else 2^(e-7). Zero gives
+// X = 1. Clamped to [1, 253] so 2^(127 - byte) is a normal float.
+__device__ __forceinline__ uint32_t e8m0_of(float amax) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, amax);
+  const int eb = (int)((u >> 23) & 0xFF);
+  int byte = eb - 8 + ((u & 0x7FFFFF) > 0x600000 ? 1 : 0);
+  byte = eb == 0 ? 127 : byte;
+  return (uint32_t)__builtin_amdgcn_fmed3f((float)byte, 1.0f, 253.0f);
+}
+__device__ __forceinline__ float inv_scale(uint32_t byte) { return __builtin_bit_cast(float, (254u - byte) << 23); }
+
+template <bool CAUSAL, int EMU16>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+                      const uint8_t* __restrict__ QS, const uint8_t* __restrict__ KS, const uint8_t* __restrict__ VS,
+                      __bf16* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats, int H,
+                      int Nq, int Nk, int n_qt, float c, float tau) {
+  __shared__ __attribute__((aligned(1024))) char kb0[kTile];
+  __shared__ __attribute__((aligned(1024))) char kb1[kTile];
+  __shared__ __attribute__((aligned(1024))) char vb0[kTile];
+  __shared__ __attribute__((aligned(1024))) char vb1[kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, l32 = lane & 31;
+
+  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int bh = logical / n_qt;
+  int qt = logical - bh * n_qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;
+  const int q0 = qt * kBM;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + l32;
+  const bool wave_rows = qw0 < Nq;  // Nq is a multiple of 32: a wave's rows are all valid or all past the end
+  const size_t qbase = (size_t)bh * Nq * kD;
+  const size_t kbase = (size_t)bh * Nk * kD;
+  const int nqb = Nq / 32, nkb = Nk / 32;
+
+  // ---- per-lane constants --------------------------------------------------
+  const int krow = key_of_row(l32);
+  uint32_t koff[2][2];  // [d step s][which 16-byte half]
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) koff[s][w] = krow * kRB + 16 * ((4 * s + 2 * w + hh) ^ swz_k(krow));
+  uint32_t voff[4];  // per d block: this lane's 8-byte slot of a transpose read, row offset 0
+  {
+    const int L = lane & 15, gidx = (lane >> 4) & 1;
+    const int vr = 16 * hh + (L >> 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int cch = 2 * db + gidx;
+      voff[db] = vr * kRB + 16 * (cch ^ swz_v(vr)) + 8 * (L & 1);
+    }
+  }
+  uint32_t kld[kLoads], vld[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int pos = 64 * (wave + kWaves * i) + lane;
+    const int r = pos / kCH, p = pos % kCH;
+    kld[i] = r * kRB + 16 * (p ^ swz_k(r));
+    vld[i] = r * kRB + 16 * (p ^ swz_v(r));
+  }
+  const int nrec = Nk * kRB;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + kbase), (short)0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + kbase), (short)0, nrec, 0x00020000);
+
+  // ---- Q operand: lane (h, n) holds Q[n][64s + 16h .. +16] and Q[n][64s + 32 + 16h .. +16]
+  i32x8 qf[2];
+  uint32_t qsc = 0x7F7F7F7Fu;
+  {
+    const uint8_t* qp = Q + qbase + (size_t)(wave_rows ? qi : 0) * kD + 16 * hh;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4 lo = wave_rows ? *(const u32x4*)(qp + 64 * s) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 hi = wave_rows ? *(const u32x4*)(qp + 64 * s + 32) : u32x4{0u, 0u, 0u, 0u};
+      qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    if (wave_rows) qsc = *(const uint32_t*)(QS + ((size_t)bh * nqb + qw0 / 32) * 4);
+  }
+  // byte 2s of (qsc >> 8h) is the scale of d block 2s + h: op_sel picks byte 2s
+  const int qscale = (int)(qsc >> (8 * hh));
+
+  const int kend = CAUSAL ? min(Nk, q0 + kBM) : Nk;
+  const int n_kt = (kend + kBN - 1) / kBN;
+
+  floatx16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = floatx16{};
+  float m_run = kNegInf, l_run = 0.0f;
+  unsigned long long cnt[4] = {0, 0, 0, 0};
+
+  auto load_tiles = [&](int t, char* kd, char* vd) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int slot = 1024 * (wave + kWaves * i);
+      dma16(rk, kd + slot, kld[i], (uint32_t)t * kTile);
+      dma16(rv, vd + slot, vld[i], (uint32_t)t * kTile);
+    }
+  };
+
+  auto scale_word = [&](const uint8_t* base, int blk, int nblk) __attribute__((always_inline)) -> uint32_t {
+    return blk < nblk ? *(const uint32_t*)(base + (size_t)blk * 4) : 0x7F7F7F7Fu;
+  };
+
+  auto compute = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
+    const int k0 = t * kBN;
+    if ((CAUSAL && k0 > qw0 + 31) || !wave_rows) return;  // wave-uniform: nothing to add
+    const uint8_t* ksb = KS + (size_t)bh * nkb * 4;
+    const uint8_t* vsb = VS + (size_t)bh * nkb * 4;
+    const uint32_t kw0 = scale_word(ksb, 2 * t, nkb), kw1 = scale_word(ksb, 2 * t + 1, nkb);
+    const uint32_t vw0 = scale_word(vsb, 2 * t, nkb), vw1 = scale_word(vsb, 2 * t + 1, nkb);
+    const int kscale[2] = {(int)(kw0 >> (8 * hh)), (int)(kw1 >> (8 * hh))};
+    const int vscale = (int)(hh ? vw1 : vw0);  // lane half h supplies key block 2t + h; op_sel picks d block
+
+    // S^T = K Q^T
+    floatx16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = floatx16{};
+      const char* kp = ks + kb * 32 * kRB;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4 lo = *(const u32x4*)(kp + koff[st][0]);
+        const u32x4 hi = *(const u32x4*)(kp + koff[st][1]);
+        const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        if (st == 0)
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[0], s[kb], 0, 0, 0, kscale[kb], 0, qscale);
+        else
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[1], s[kb], 0, 0, 2, kscale[kb], 2, qscale);
+      }
+    }
+
+    if ((CAUSAL && k0 + kBN - 1 > qw0) || (k0 + kBN > Nk)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 32 * kb + 16 * hh + e;
+          if (key >= Nk || (CAUSAL && key > qi)) s[kb][e] = kNegInf;
+        }
+    }
+
+    // block maxima (reused for the P scales) and the row max
+    const float bm0 = pl_max_halves(max16(s[0]));
+    const float bm1 = pl_max_halves(max16(s[1]));
+    const float mx = __builtin_fmaxf(bm0, bm1);
+    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float acc = (m_run - m_new) * c;
+    const bool seen = mx > kNegInf;
+    const bool commit = seen && !(acc >= -tau);
+    const float alpha = commit ? exp2_hw(acc) : 1.0f;
+    if (stats) {
+      const bool step = seen && (m_run > kNegInf) && hh == 0;
+      const unsigned long long bs = __builtin_amdgcn_ballot_w64(step);
+      const unsigned long long br = __builtin_amdgcn_ballot_w64(step && commit);
+      cnt[0] += __builtin_popcountll(bs);
+      cnt[1] += __builtin_popcountll(br);
+      cnt[2] += bs != 0;
+      cnt[3] += br != 0;
+    }
+    m_run = commit ? m_new : m_run;
+    if (__builtin_amdgcn_ballot_w64(commit)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+    const float mc = (m_run > kNegInf) ? m_run * c : 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = exp2_sel<EMU16>(__builtin_fmaf(s[kb][e], c, -mc), e);
+    l_run = __builtin_fmaf(l_run, alpha, sum16(s[0]) + sum16(s[1]));
+
+    // P -> e4m3 per 32-key block; the block amax from the reused block max
+    const uint32_t sb0 = e8m0_of(exp2_hw(__builtin_fmaf(bm0, c, -mc)));
+    const uint32_t sb1 = e8m0_of(exp2_hw(__builtin_fmaf(bm1, c, -mc)));
+    const float inv0 = inv_scale(sb0), inv1 = inv_scale(sb1);
+    i32x8 pq;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      int lo = 0, hi = 0;
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * w] * inv0, s[0][4 * w + 1] * inv0, lo, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * w + 2] * inv0, s[0][4 * w + 3] * inv0, lo, true);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * w] * inv1, s[1][4 * w + 1] * inv1, hi, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * w + 2] * inv1, s[1][4 * w + 3] * inv1, hi, true);
+      pq[w] = lo;
+      pq[4 + w] = hi;
+    }
+    const int pscale = (int)(hh ? sb1 : sb0);
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      i32x8 a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {  // keys 32*(r/2) + 16h + 8*(r%2) .. +8
+        const char* vp = vs + voff[db] + (32 * (r >> 1) + 8 * (r & 1)) * kRB;
+        const intx2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2*)vp);
+        a[2 * r] = v[0];
+        a[2 * r + 1] = v[1];
+      }
+      switch (db) {
+        case 0: o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[0], 0, 0, 0, vscale, 0, pscale); break;
+        case 1: o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[1], 0, 0, 1, vscale, 0, pscale); break;
+        case 2: o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[2], 0, 0, 2, vscale, 0, pscale); break;
+        default: o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[3], 0, 0, 3, vscale, 0, pscale); break;
+      }
+    }
+  };
+
+  load_tiles(0, kb0, vb0);
+  wait_own_loads();
+  __syncthreads();
+  for (int t = 0; t < n_kt; t += 2) {
+    if (t + 1 < n_kt) load_tiles(t + 1, kb1, vb1);
+    compute(t, kb0, vb0);
+    wait_own_loads();
+    __syncthreads();
+    if (t + 1 >= n_kt) break;
+    if (t + 2 < n_kt) load_tiles(t + 2, kb0, vb0);
+    compute(t + 1, kb1, vb1);
+    wait_own_loads();
+    __syncthreads();
+  }
+
+  const float l_tot = pl_sum_halves(l_run);
+  const float inv = 1.0f / l_tot;
+  if (wave_rows) {
+    __bf16* op = O + qbase + (size_t)qi * kD + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[db][4 * g + r] * inv);
+        *(bf16x4*)(op + 32 * db + 8 * g) = w;
+      }
+    if (hh == 0) LSE[(size_t)bh * Nq + qi] = (m_run * c + __builtin_log2f(l_tot)) * 0.693147180559945309f;
+  }
+  if (stats && lane == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) atomicAdd(stats + i, cnt[i]);
+  }
+}
+
+template <bool CAUSAL, int EMU16>
+hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+  const int n_qt = (a.Nq + kBM - 1) / kBM;
+  const long long grid = (long long)a.B * a.H * n_qt;
+  hipLaunchKernelGGL((fwd_mxfp8_kernel<CAUSAL, EMU16>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                     (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_scale, a.k_scale, a.v_scale,
+                     (__bf16*)a.o, a.lse, a.stats, a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau);
+  return hipGetLastError();
+}
+
+template <bool CAUSAL>
+hipError_t launch_mode(const FwdArgs& a, hipStream_t stream) {
+  switch (a.emu16) {
+    case 0: return launch<CAUSAL, 0>(a, stream);
+    case 1: return launch<CAUSAL, 1>(a, stream);
+    case 2: return launch<CAUSAL, 2>(a, stream);
+    case 3: return launch<CAUSAL, 3>(a, stream);
+    case 4: return launch<CAUSAL, 4>(a, stream);
+    case 8: return launch<CAUSAL, 8>(a, stream);
+    case 16: return launch<CAUSAL, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_mxfp8(const FwdArgs& a, hipStream_t stream) {
+  if (a.d != kD) return hipErrorInvalidValue;
+  return a.causal ? launch_mode<true>(a, stream) : launch_mode<false>(a, stream);
+}
 
 }  // namespace attn

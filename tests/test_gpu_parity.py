@@ -84,7 +84,7 @@ def _sample_rows(Nq, rng):
     return np.unique(np.concatenate([fixed, rng.integers(0, Nq, 18)]).clip(0, Nq - 1))
 
 
-@pytest.mark.parametrize("name", FP_WORKLOADS)
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
 def test_full_size_sampled_parity(attn, name):
     """Full workload sizes in the bench's launch configuration; the oracle
     recomputes a sample of rows (tile edges plus random rows) of a few heads."""
@@ -234,3 +234,67 @@ def test_rescale_counts_match_oracle(attn, tau, causal):
     assert abs(st[3] - groups_ref) <= max(2, 0.01 * groups_ref)
     if tau == 0.0:
         assert st[1] > 0
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (e4m3 + one E8M0 per 32x32 block; P re-quantised per 32 keys)
+# ---------------------------------------------------------------------------
+MX = WORKLOADS["mxfp8_b2h16_n8192_d128"]
+E4M3_REL = 2.0 ** -4     # e4m3 keeps 3 mantissa bits: relative rounding error <= 2^-4
+
+
+def _mx_bound(x, o_ref, causal, mode):
+    """Per-row bound for rows too short to average out P's e4m3 rounding:
+    each P_j carries a relative error <= 2^-4 in the numerator only (l sums
+    the float32 P), so |dO_i| <= 2^-4 * max_j |v_j| over the keys row i sees,
+    plus the software-exp2 term when it is used."""
+    v = x["v64"]
+    B, H, Nq, _ = o_ref.shape
+    out = np.empty((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            for i in range(Nq):
+                vv = v[b, h, : i + 1] if causal else v[b, h]
+                out[b, h, i] = E4M3_REL * np.abs(vv).max()
+                if mode != "hw":
+                    out[b, h, i] += 2 * EX2_EMU_MAX_REL * np.abs(vv - o_ref[b, h, i]).max()
+    return out
+
+
+@pytest.mark.parametrize("mode", ["hw", "mix", "emu"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mxfp8_small_parity(attn, mode, causal):
+    announce(f"mxfp8 small causal={causal} mode={mode}")
+    x = make_inputs(MX, B=1, H=2, Nq=320, Nk=352)   # 3 query tiles; 5.5 key tiles
+    o_ref, lse_ref = attention_f64(x["q64"], x["k64"], x["v64"], causal=causal)
+    o, lse = run_fwd(attn, to_device(x), causal, mode, 0.0)
+    tol_rows = _mx_bound(x, o_ref, causal, mode) if causal else None
+    _compare(o, lse, o_ref, lse_ref, "mxfp8", f"mxfp8 causal={causal} {mode}", tol_rows)
+
+
+def test_mxfp8_tau_zero_and_eight_agree(attn):
+    x = make_inputs(MX, B=1, H=2, Nq=256, Nk=1024)
+    dev = to_device(x)
+    o0, l0 = run_fwd(attn, dev, False, "hw", 0.0)
+    o8, l8 = run_fwd(attn, dev, False, "hw", 8.0)
+    assert np.abs(host64(o0) - host64(o8)).max() <= TOL_O["mxfp8"]
+    assert np.abs(host64(l0) - host64(l8)).max() <= TOL_LSE
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 32, 32), (1, 2, 64, 96), (2, 1, 96, 32)])
+def test_mxfp8_edge_shapes(attn, shape):
+    B, H, Nq, Nk = shape
+    x = make_inputs(MX, B=B, H=H, Nq=Nq, Nk=Nk)
+    for causal in (False, True):
+        o_ref, lse_ref = attention_f64(x["q64"], x["k64"], x["v64"], causal=causal)
+        o, lse = run_fwd(attn, to_device(x), causal, "hw", 0.0)
+        _compare(o, lse, o_ref, lse_ref, "mxfp8", f"mxfp8 edge {shape} causal={causal}",
+                 _mx_bound(x, o_ref, causal, "hw"))
+
+
+def test_mxfp8_rejects_bad_shapes(attn):
+    import torch
+    q = torch.zeros(1, 1, 48, 128, dtype=torch.uint8, device="cuda")
+    s = torch.zeros(1, 1, 1, 4, dtype=torch.uint8, device="cuda")
+    with pytest.raises(attn.AttnError, match="ATTN_E_SHAPE"):
+        attn.fwd(q, q, q, q_scale=s, k_scale=s, v_scale=s)
