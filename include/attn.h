@@ -44,8 +44,10 @@ extern "C" {
 enum {
   ATTN_OK = 0,
   ATTN_E_NULLPTR = -1,   /* a required pointer is NULL                               */
-  ATTN_E_SHAPE = -2,     /* B, H, Nq < 0; Nk < 1 with work to do; sizes too large;
-                            MXFP8 with Nq or Nk not a multiple of 32                   */
+  ATTN_E_SHAPE = -2,     /* B, H, Nq < 0; Nk < 1 with work to do; sizes too large
+                            (Nq or Nk above 2^30, or one (b, h) slice of Q, K or V
+                            of 2 GiB or more); MXFP8 with Nq or Nk not a
+                            multiple of 32                                            */
   ATTN_E_HEADDIM = -3,   /* d not supported for the dtype (f32/bf16: 64 or 128;
                             MXFP8: 128)                                                */
   ATTN_E_DTYPE = -4,     /* unknown dtype code                                         */

@@ -4,6 +4,7 @@
 // without a GPU.
 #include "attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -89,6 +90,12 @@ int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void
   const long long n_qt = (Nq + 127) / 128;
   if ((long long)B * H * n_qt > 0x7FFFFFFFLL || Nq > (1 << 30) || Nk > (1 << 30))
     return fail(ATTN_E_SHAPE, "sizes too large (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
+  // The kernels address one (batch, head) slice of Q, K or V through a buffer
+  // resource with 32-bit byte offsets, up to one key tile past the end.
+  const long long esize = dtype == ATTN_F32 ? 4 : dtype == ATTN_BF16 ? 2 : 1;
+  if (((long long)std::max(Nq, Nk) + 256) * d * esize > 0x7FFFFFFFLL)
+    return fail(ATTN_E_SHAPE, "one (batch, head) slice of Q, K or V must stay under 2 GiB (Nq=%d Nk=%d d=%d)", Nq,
+                Nk, d);
   if (dtype == ATTN_MXFP8_E4M3 && (Nq % 32 != 0 || Nk % 32 != 0))
     return fail(ATTN_E_SHAPE, "MXFP8 needs Nq and Nk to be multiples of 32 (Nq=%d Nk=%d)", Nq, Nk);
   if (!Q || !K || !V || !O || !LSE) return fail(ATTN_E_NULLPTR, "Q, K, V, O and LSE must be non-NULL");

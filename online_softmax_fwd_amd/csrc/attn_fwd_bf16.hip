@@ -92,11 +92,13 @@ __device__ __forceinline__ int key_of_row(int m) {
 __device__ __forceinline__ void wait_own_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // One wave-wide 16-byte-per-lane DMA from a buffer into LDS: lane i's 16 bytes
-// at byte voff + soff of the buffer land at lds + 16 * i. (Kept in a device
-// function: the host compilation pass must not see this builtin in a kernel
-// body.)
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
+// at byte off of the buffer land at lds + 16 * i; bytes at or past the
+// buffer's record count arrive as zeros (the range check covers the whole
+// offset; it is passed per lane and the scalar offset stays 0). (Kept in a
+// device function: the host compilation pass must not see this builtin in a
+// kernel body.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, off, 0, 0, 0);
 }
 
 // Cross-half reductions with v_permlane32_swap: it exchanges the upper half of
@@ -305,9 +307,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int i = 0; i < C::LOADS; ++i) {
       const int slot = 1024 * (wave + 8 * i);
       if (j + 1 < T)
-        dma16(rk, kdst + slot, kld[i], (uint32_t)(j + 1) * C::TILE);
+        dma16(rk, kdst + slot, kld[i] + (uint32_t)(j + 1) * C::TILE);
       if (j < T)
-        dma16(rv, vdst + slot, vld[i], (uint32_t)j * C::TILE);
+        dma16(rv, vdst + slot, vld[i] + (uint32_t)j * C::TILE);
     }
   };
 
@@ -384,7 +386,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // prologue: K_0 by every wave
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) dma16(rk, kb0 + 1024 * (wave + 8 * i), kld[i], 0);
+  for (int i = 0; i < C::LOADS; ++i) dma16(rk, kb0 + 1024 * (wave + 8 * i), kld[i]);
   wait_own_loads();
   __syncthreads();
   if (group == 1) {

@@ -69,8 +69,14 @@ __device__ __forceinline__ int swz_v(int r) { return ((r >> 1) & 3) << 1; }
 
 __device__ __forceinline__ void wait_own_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
+// One wave-wide 16-byte-per-lane DMA from a buffer into LDS: lane i's 16 bytes
+// at byte off of the buffer land at lds + 16 * i; bytes at or past the
+// buffer's record count arrive as zeros (the range check covers the whole
+// offset; it is passed per lane and the scalar offset stays 0). (Kept in a
+// device function: the host compilation pass must not see this builtin in a
+// kernel body.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, off, 0, 0, 0);
 }
 
 __device__ __forceinline__ float pl_max_halves(float x) {
@@ -204,8 +210,8 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int slot = 1024 * (wave + kWaves * i);
-      dma16(rk, kd + slot, kld[i], (uint32_t)t * kTile);
-      dma16(rv, vd + slot, vld[i], (uint32_t)t * kTile);
+      dma16(rk, kd + slot, kld[i] + (uint32_t)t * kTile);
+      dma16(rv, vd + slot, vld[i] + (uint32_t)t * kTile);
     }
   };
 

@@ -72,6 +72,8 @@ def _call(lib, **kw):
     (dict(dtype=2, Nq=100), -2),      # MXFP8 needs multiples of 32
     (dict(dtype=2), -1),              # MXFP8 needs scales
     (dict(Nq=1 << 31 - 1, B=1 << 20), -2),
+    (dict(Nk=1 << 23), -2),           # one bf16 d=128 K/V slice of 2 GiB or more
+    (dict(Nq=1 << 24, d=64, dtype=0), -2),  # f32 Q slice of 4 GiB
 ])
 def test_validation_errors(lib, kw, code):
     assert _call(lib, **kw) == code
