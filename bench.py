@@ -14,7 +14,11 @@ Prints ONE JSON line. Besides the contract fields it carries
   roofline      for the dominant kernel (the non-causal launch): algorithmic
                 FLOPs per launch / its mean duration from HIP events recorded
                 on the launch stream inside the timed region, against the
-                dense bf16 MFMA peak of MI355X (2.5 PFLOP/s)
+                dense bf16 MFMA peak of MI355X (2.5 PFLOP/s); "traffic" is the
+                calibrated HBM byte count per launch from rocprofv3 counters
+                (null when no counter run covers these kernel sources)
+  rescale       lagging-max rescale counts per mode, from one counting launch
+                (attn_fwd_stats) outside the timed region
   cpu_baseline  the float64 oracle timed on a bounded sample of the same
                 workload on the host cores (rank 0, N=1 only)
 """
@@ -34,10 +38,33 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}   # MI355X dense MFMA, published
 MODE_CODES = {"hw": 0, "emu": 1, "mix": 2}
 DEFAULT_WORKLOAD = "bf16_b4h16_n4096_d128"
-# Measured HBM-traffic calibration (rocprofv3 FETCH_SIZE / WRITE_SIZE on a plain
-# copy of known size, and on the non-causal kernel at the default workload);
-# None until a counter run has been taken for the kernel as it stands.
-TRAFFIC_BYTES_PER_LAUNCH = None
+# HBM traffic of one non-causal launch of the default workload, from two
+# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch, --calib-copy-mib 256). Calibrated on a plain 256 MiB device copy in
+# the same runs: FETCH_SIZE read 131088.5 KiB for 262144 KiB moved (x2.0),
+# WRITE_SIZE read 262144 KiB (x1.0). Valid only for the kernel sources it was
+# taken on (first 16 hex digits of their SHA-256); any edit turns it off.
+TRAFFIC = {
+    "workload": "bf16_b4h16_n4096_d128",
+    "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "dc5d5579a6a4855c",
+                "online_softmax_fwd_amd/csrc/attn_device.h": "7d2b3a40c400162f"},
+    "fetch_kib_raw": 98454.7, "fetch_scale": 2.0,
+    "write_kib_raw": 66560.0, "write_scale": 1.0,
+}
+
+
+def traffic_bytes(w):
+    """Calibrated HBM bytes per launch of the dominant kernel, or None when no
+    counter run covers this workload and these kernel sources."""
+    import hashlib
+    if w.name != TRAFFIC["workload"]:
+        return None
+    for rel, digest in TRAFFIC["sources"].items():
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
+                return None
+    kib = TRAFFIC["fetch_kib_raw"] * TRAFFIC["fetch_scale"] + TRAFFIC["write_kib_raw"] * TRAFFIC["write_scale"]
+    return int(round(kib * 1024))
 
 
 def parse():
@@ -59,22 +86,27 @@ def flops_of(w, causal: bool) -> float:
     return f / 2 if causal else f
 
 
-def cpu_baseline(w, causal_modes):
-    """The float64 oracle, untuned, on one batch entry's heads of the workload."""
+def cpu_baseline(w, causal_modes, flop_budget=1.2e12):
+    """The float64 oracle, untuned, on the workload's (batch, head) slices, as
+    many of them as fit a FLOP budget of about 10-30 s of host time (all of
+    them for the default workload)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from attn_inputs import make_inputs
     from oracle import attention_f64
 
-    heads = min(w.H, 16)
-    x = make_inputs(w, B=1, H=heads)
+    per_slice = sum(4.0 * w.Nq * w.Nk * w.d for _ in causal_modes)   # the oracle forms the full S either way
+    n_bh = int(min(w.B * w.H, max(1, flop_budget // per_slice)))
+    if n_bh == w.B * w.H:
+        x, what = make_inputs(w), f"the whole workload (B={w.B} H={w.H})"
+    else:
+        x, what = make_inputs(w, B=1, H=n_bh), f"{n_bh} of its {w.B * w.H} (batch, head) slices"
     flops = 0.0
     t0 = time.perf_counter()
     for causal in causal_modes:
         attention_f64(x["q64"], x["k64"], x["v64"], causal=causal)
-        f = 4.0 * heads * w.Nq * w.Nk * w.d
-        flops += f / 2 if causal else f
+        flops += n_bh * 4.0 * w.Nq * w.Nk * w.d / (2 if causal else 1)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
@@ -82,8 +114,8 @@ def cpu_baseline(w, causal_modes):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"B=1 H={heads} of the workload (Nq=Nk={w.Nq}, d={w.d}), causal modes {list(causal_modes)}; "
-                  f"float64 numpy, one-shot softmax, full S computed even when causal; {dt:.1f} s",
+        "sample": f"{what}, Nq=Nk={w.Nq} d={w.d}, causal modes {list(causal_modes)}; float64 numpy one-shot "
+                  f"softmax (it forms the full S even when causal; FLOPs counted as for the GPU); {dt:.1f} s",
         "seconds": round(dt, 2),
     }
 
@@ -212,9 +244,18 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": TRAFFIC_BYTES_PER_LAUNCH,
+            "traffic": traffic_bytes(w),
+            "traffic_unit": "bytes per launch (HBM read + write)",
         },
     }
+    # lagging-max rescales, one extra launch per mode outside the timed region
+    rescale = {}
+    for c in w.causal:
+        _, _, st = attn.fwd_stats(q, k, v, causal=c, exp2_mode=mode, tau=tau, stream=stream, **scales)
+        rescale["causal" if c else "noncausal"] = {
+            "row_tile_steps": st[0], "row_rescales": st[1], "wave_tile_steps": st[2], "wave_rescales": st[3],
+            "row_frac": round(st[1] / max(st[0], 1), 6), "wave_frac": round(st[3] / max(st[2], 1), 6)}
+    result["rescale"] = rescale
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, w.causal)
     print(json.dumps(result), flush=True)
