@@ -70,8 +70,8 @@ def traffic_bytes(w):
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--exp2-mode", default=None, help="override the workload's exp2 mode (hw, emu, mix, mixK)")
     p.add_argument("--tau", type=float, default=None)

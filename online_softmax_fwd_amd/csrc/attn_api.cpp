@@ -29,22 +29,24 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Emulated share of P (16ths) for ATTN_EXP2_MIX, keyed by (dtype, d, causal).
 // The first page reports the Blackwell kernel's shares ("FlashAttention-4's
 // Softmax Tricks", section "The emulated exp2": 18.75 % non-causal d=128,
-// 12.5 % causal d=128, 25 % FP8). The bf16 entries here are the fastest shares
-// measured on MI355X with this library's kernels (sweep over 0, 1, 2, 3, 4, 8
-// and 16 sixteenths at B=4 H=16 N=4096 d=128 and B=2 H=32 N=8192 d=64):
-// non-causal d=128 2/16, causal d=128 0/16, causal d=64 1/16; MXFP8 at
-// B=2 H=16 N=8192 d=128: 2/16. The float32 entry is the page's value rounded
-// to a supported share.
+// 12.5 % causal d=128, 25 % FP8), chosen there because the exponential unit
+// is a separate, narrow pipeline. On gfx950 v_exp_f32 issues on the vector ALU
+// itself, and the software exp2 costs 7 more VALU instructions per value
+// (SQ_INSTS_VALU per launch), so moving work there only pays if the ALU has
+// idle issue slots. The entries are the fastest shares measured on MI355X
+// with these kernels (HIP-event medians after a 2 s warm-up, shares 0, 1, 2
+// and 4 sixteenths): bf16 d=128 non-causal and causal at B=4 H=16 N=4096 and
+// bf16 d=64 causal at B=2 H=32 N=8192 are fastest all-hardware; MXFP8
+// non-causal at B=2 H=16 N=8192 ties at 0 and 1 sixteenth (1/16 kept), causal
+// is fastest at 0. The float32 kernel follows the bf16 entries.
 int mix_table(int dtype, int d, int causal) {
   if (d != 64 && d != 128) return -1;
   switch (dtype) {
     case ATTN_BF16:
-      if (d == 128) return causal ? 0 : 2;
-      return 1;
     case ATTN_F32:
-      return 2;
+      return 0;
     case ATTN_MXFP8_E4M3:
-      return 2;
+      return causal ? 0 : 1;
     default:
       return -1;
   }

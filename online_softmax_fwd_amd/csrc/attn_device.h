@@ -76,4 +76,55 @@ __device__ __forceinline__ int xcd_logical_id(int wg, int n) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
+// Causal query tiles differ in length: tile qt of a head needs its first
+// qt+1 tiles' worth of keys. When the heads split evenly over the 8 XCDs, XCD
+// x takes the heads bh = x (mod 8), all of whose tiles therefore share that
+// XCD's L2, and hands them to its compute units longest first (all heads'
+// last tiles, then their second-to-last, ...), so the short tiles fill the
+// gaps at the end instead of a long tile starting last. Otherwise the tiles
+// follow xcd_logical_id, longest first within each head. Either way the map
+// from workgroup to (head, tile) is a bijection.
+__device__ __forceinline__ void causal_tile_of(int wg, int n_wg, int n_qt, int& bh, int& qt) {
+  const int n_bh = n_wg / n_qt;
+  if ((n_bh & 7) == 0) {
+    const int xcd = wg & 7, slot = wg >> 3, per = n_bh >> 3;
+    qt = n_qt - 1 - slot / per;
+    bh = (slot % per) * 8 + xcd;
+  } else {
+    const int logical = xcd_logical_id(wg, n_wg);
+    bh = logical / n_qt;
+    qt = n_qt - 1 - (logical - bh * n_qt);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K/V tile DMA: buffer_load_dwordx4 ... lds copies 16 bytes per lane from a
+// buffer straight into LDS (lane i's bytes land at the LDS address in M0 plus
+// 16 * i), with no VGPR staging. The buffer resource makes it a raw byte
+// buffer of nbytes: offsets are 32-bit and range-checked (the check covers
+// the whole offset), and bytes at or past nbytes arrive as zeros.
+//
+// The instruction is written as inline asm rather than through the compiler
+// builtin: the compiler cannot tell which LDS buffer a DMA writes, so before
+// an LDS read it waits for every DMA still in flight, whichever buffer it
+// targets, which would serialise the prefetch of the next tile with the reads
+// of the current one. The kernels order DMA and reads themselves: the issuing
+// wave waits on its vector-memory counter (s_waitcnt vmcnt) before the
+// workgroup barrier that precedes the reads, and no DMA targets a buffer
+// before the barrier after its last read. The asm sets M0 itself; no compiler
+// builtin that depends on M0 runs in these kernels.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 raw_buffer_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t p = (uint64_t)base;
+  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, nbytes, 0x00020000u};
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(const u32x4& rs, const char* lds, uint32_t off) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(rs)
+               : "memory");
+}
+
 }  // namespace attn

@@ -53,7 +53,6 @@ namespace attn {
 namespace {
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 template <int D_, int BN_, int NW_>
@@ -91,15 +90,16 @@ __device__ __forceinline__ int key_of_row(int m) {
 
 __device__ __forceinline__ void wait_own_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// One wave-wide 16-byte-per-lane DMA from a buffer into LDS: lane i's 16 bytes
-// at byte off of the buffer land at lds + 16 * i; bytes at or past the
-// buffer's record count arrive as zeros (the range check covers the whole
-// offset; it is passed per lane and the scalar offset stays 0). (Kept in a
-// device function: the host compilation pass must not see this builtin in a
-// kernel body.)
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, off, 0, 0, 0);
-}
+// Workgroup barrier without a memory fence. __syncthreads() releases at
+// workgroup scope, which makes every wave wait for all of its outstanding
+// vector-memory operations, tile DMAs included, at every barrier. Here each
+// wave waits for its own DMA explicitly (wait_own_loads) at the barrier before
+// the data is read, so the barriers in between do not stall on loads still in
+// flight. The LDS reads a wave issued must have returned before it passes (a
+// later DMA may overwrite the buffer), and the asm's memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 
 // Cross-half reductions with v_permlane32_swap: it exchanges the upper half of
 // one register with the lower half of the other, so (r[0], r[1]) is
@@ -242,10 +242,14 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int group = wave >> 2;
   const int hh = lane >> 5, l32 = lane & 31;
 
-  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = logical / n_qt;
-  int qt = logical - bh * n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
+  int bh, qt;
+  if (CAUSAL) {
+    causal_tile_of(blockIdx.x, gridDim.x, n_qt, bh, qt);
+  } else {
+    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+    bh = logical / n_qt;
+    qt = logical - bh * n_qt;
+  }
   const int q0 = qt * C::BM;
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + l32;
@@ -274,8 +278,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   }
   const int nrec = Nk * C::RB;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + kbase), (short)0, nrec, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + kbase), (short)0, nrec, 0x00020000);
+  const u32x4 rk = raw_buffer_rsrc(K + kbase, (uint32_t)nrec);
+  const u32x4 rv = raw_buffer_rsrc(V + kbase, (uint32_t)nrec);
 
   // ---- Q as the B operand: lane (h, n) holds Q[n][16s + 8h .. +8] -----------
   bf16x8 qf[D / 16];
@@ -375,11 +379,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     if (group == 0) load_tiles(j, knxt, vcur);
     mfma_phase(do_pv, do_qk, kcur, vprv);
     if (group == 1) wait_own_loads();
-    __syncthreads();
+    block_sync();
     if (group == 1) load_tiles(j + 1, kcur, vprv);
     if constexpr (decltype(do_qk)::value) valu_phase(j);
     if (group == 0) wait_own_loads();
-    __syncthreads();
+    block_sync();
   };
   using Y = std::true_type;
   using N = std::false_type;
@@ -388,11 +392,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) dma16(rk, kb0 + 1024 * (wave + 8 * i), kld[i]);
   wait_own_loads();
-  __syncthreads();
+  block_sync();
   if (group == 1) {
     // group 1's share of K_1 and V_0 goes out with group 0's, at half-phase 0
     load_tiles(0, kb1, vb0);
-    __syncthreads();
+    block_sync();
   }
   step(0, N{}, Y{}, kb0, kb1, vb1, vb0);
   int j = 1;
@@ -409,7 +413,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     step(j, Y{}, N{}, kb1, kb0, vb0, vb1);
   else
     step(j, Y{}, N{}, kb0, kb1, vb1, vb0);
-  if (group == 0) __syncthreads();
+  if (group == 0) block_sync();
 
   // ---- epilogue: O / l, LSE -------------------------------------------------
   const float l_tot = pl_sum_halves(l_run);

@@ -46,10 +46,14 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
-  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = logical / n_qt;
-  int qt = logical - bh * n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;
+  int bh, qt;
+  if (CAUSAL) {
+    causal_tile_of(blockIdx.x, gridDim.x, n_qt, bh, qt);
+  } else {
+    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+    bh = logical / n_qt;
+    qt = logical - bh * n_qt;
+  }
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kQW;
   const int qi = qw0 + l32;

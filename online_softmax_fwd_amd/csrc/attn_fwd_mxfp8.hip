@@ -42,7 +42,6 @@ namespace attn {
 namespace {
 
 typedef int intx2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) intx2 lds_intx2;
 
 constexpr int kD = 128;
@@ -69,15 +68,6 @@ __device__ __forceinline__ int swz_v(int r) { return ((r >> 1) & 3) << 1; }
 
 __device__ __forceinline__ void wait_own_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// One wave-wide 16-byte-per-lane DMA from a buffer into LDS: lane i's 16 bytes
-// at byte off of the buffer land at lds + 16 * i; bytes at or past the
-// buffer's record count arrive as zeros (the range check covers the whole
-// offset; it is passed per lane and the scalar offset stays 0). (Kept in a
-// device function: the host compilation pass must not see this builtin in a
-// kernel body.)
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, off, 0, 0, 0);
-}
 
 __device__ __forceinline__ float pl_max_halves(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -140,10 +130,14 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, l32 = lane & 31;
 
-  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = logical / n_qt;
-  int qt = logical - bh * n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;
+  int bh, qt;
+  if (CAUSAL) {
+    causal_tile_of(blockIdx.x, gridDim.x, n_qt, bh, qt);
+  } else {
+    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+    bh = logical / n_qt;
+    qt = logical - bh * n_qt;
+  }
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + l32;
@@ -178,8 +172,8 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
     vld[i] = r * kRB + 16 * (p ^ swz_v(r));
   }
   const int nrec = Nk * kRB;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + kbase), (short)0, nrec, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + kbase), (short)0, nrec, 0x00020000);
+  const u32x4 rk = raw_buffer_rsrc(K + kbase, (uint32_t)nrec);
+  const u32x4 rv = raw_buffer_rsrc(V + kbase, (uint32_t)nrec);
 
   // ---- Q operand: lane (h, n) holds Q[n][64s + 16h .. +16] and Q[n][64s + 32 + 16h .. +16]
   i32x8 qf[2];
