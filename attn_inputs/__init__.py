@@ -24,7 +24,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "make_inputs", "bf16_bits", "bf16_bits_to_f32",
     "e4m3_decode_table", "e4m3_encode", "e8m0_for_amax", "mx_quantize",
-    "mx_dequantize",
+    "mx_dequantize", "make_score_inputs",
 ]
 
 
@@ -220,3 +220,16 @@ def _spike(tensors, vals, dtype, b, h, idx, gain):
         tensors["k"][b, h, idx] = bf16_bits(f)
     else:
         raise ValueError("spikes are defined for f32 and bf16 workloads")
+
+
+def make_score_inputs(sigma: float, seed: int, rows: int = 256, keys: int = 8192, d: int = 128):
+    """Scores and values for the P-cast study of "FlashAttention-4's Softmax
+    Tricks" (section "Where 'exact' breaks: P in FP8"): 256 rows x 8192 keys of
+    iid N(0, sigma^2) scores in log2 units, drawn first, then V [keys, d] iid
+    N(0, 1), both float64 standard normals from default_rng(seed). The page
+    gives the score distribution and the sizes; V's distribution and d are
+    this recipe's choice."""
+    rng = np.random.default_rng(seed)
+    scores = rng.standard_normal((rows, keys)) * sigma
+    v = rng.standard_normal((keys, d))
+    return scores, v

@@ -15,6 +15,11 @@ Contents
                        counts; never the parity reference)
   ex2_emu_deg3         float32 CPU model of the degree-3 software exp2
                        (C, built with gcc; see ex2_emu.c)
+  round_to_format      cast to bf16 / OCP E4M3 / OCP E5M2 (nearest-even,
+                       saturating)
+  lagging_max_p_cast_f64
+                       the pages' simulation of P cast to a narrow type
+                       (times 2^max_offset) under the lagging max
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 brute force at 50 digits, library routines that differ from the ones used
@@ -22,6 +27,7 @@ here, and the numbers the pages print. No function is "parity unpinned".
 """
 from .attention import attention_f64, attention_rows_f64, blockwise_f64
 from .ex2_emu import ex2_emu_deg3, build_ex2_emu
+from .p_cast import lagging_max_p_cast_f64, rel_l2, round_to_format
 
 __all__ = ["attention_f64", "attention_rows_f64", "blockwise_f64",
-           "ex2_emu_deg3", "build_ex2_emu"]
+           "ex2_emu_deg3", "build_ex2_emu", "lagging_max_p_cast_f64", "rel_l2", "round_to_format"]
