@@ -75,6 +75,8 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--exp2-mode", default=None, help="override the workload's exp2 mode (hw, emu, mix, mixK)")
     p.add_argument("--tau", type=float, default=None)
+    p.add_argument("--fp8-p", default="block", choices=["block", "e4m3", "e5m2"],
+                   help="MXFP8 workloads: P scaled per 32-key block, or times 2^8 with one fixed scale as E4M3 or E5M2")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (HBM counter calibration)")
@@ -159,6 +161,7 @@ def main():
         scales = dict(q_scale=torch.from_numpy(x["qs"]).to(dev), k_scale=torch.from_numpy(x["ks"]).to(dev),
                       v_scale=torch.from_numpy(x["vs"]).to(dev))
     del x
+    fp8 = dict(fp8_p=args.fp8_p) if w.dtype == "mxfp8" else {}
     odt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     outs = {c: (torch.empty((w.B, w.H, w.Nq, w.d), dtype=odt, device=dev),
                 torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)) for c in w.causal}
@@ -166,7 +169,7 @@ def main():
 
     def launch(causal):
         o, l = outs[causal]
-        attn.fwd(q, k, v, causal=causal, exp2_mode=mode, tau=tau, out=o, lse=l, stream=stream, **scales)
+        attn.fwd(q, k, v, causal=causal, exp2_mode=mode, tau=tau, out=o, lse=l, stream=stream, **scales, **fp8)
 
     for _ in range(args.warmup):
         for c in w.causal:
@@ -234,6 +237,7 @@ def main():
                         f"exp2 {mode}, tau={tau}",
             "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": list(w.causal),
             "exp2_mode": mode, "mix_sixteenths": mix16, "tau": tau, "seed": w.seed,
+            **({"fp8_p": args.fp8_p} if w.dtype == "mxfp8" else {}),
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
         "per_mode": per_mode,
@@ -251,7 +255,7 @@ def main():
     # lagging-max rescales, one extra launch per mode outside the timed region
     rescale = {}
     for c in w.causal:
-        _, _, st = attn.fwd_stats(q, k, v, causal=c, exp2_mode=mode, tau=tau, stream=stream, **scales)
+        _, _, st = attn.fwd_stats(q, k, v, causal=c, exp2_mode=mode, tau=tau, stream=stream, **scales, **fp8)
         rescale["causal" if c else "noncausal"] = {
             "row_tile_steps": st[0], "row_rescales": st[1], "wave_tile_steps": st[2], "wave_rescales": st[3],
             "row_frac": round(st[1] / max(st[0], 1), 6), "wave_frac": round(st[3] / max(st[2], 1), 6)}

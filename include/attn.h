@@ -52,7 +52,9 @@ enum {
                             MXFP8: 128)                                                */
   ATTN_E_DTYPE = -4,     /* unknown dtype code                                         */
   ATTN_E_EXP2MODE = -5,  /* unknown exp2_mode                                          */
-  ATTN_E_TAU = -6,       /* tau negative, above 64 or not finite                       */
+  ATTN_E_TAU = -6,       /* tau negative, above 64 or not finite; for the fixed-scale
+                            FP8 P dtypes, 8 + tau >= log2 of P's largest finite value
+                            (448 for E4M3, 57344 for E5M2)                             */
   ATTN_E_SCALE = -7,     /* scale not finite or <= 0                                   */
   ATTN_E_ALIGN = -8,     /* a tensor pointer is not 16-byte aligned (MX scale pointers:
                             4-byte aligned)                                            */
@@ -63,12 +65,23 @@ enum {
 enum {
   ATTN_F32 = 0,          /* Q, K, V, O float32                                         */
   ATTN_BF16 = 1,         /* Q, K, V, O bfloat16                                        */
-  ATTN_MXFP8_E4M3 = 2    /* Q, K, V OCP e4m3 bytes plus one E8M0 scale byte per 32x32
+  ATTN_MXFP8_E4M3 = 2,   /* Q, K, V OCP e4m3 bytes plus one E8M0 scale byte per 32x32
                             block ([B,H,N/32,d/32] uint8, V blocked along the sequence
                             with the same square blocks); O bfloat16. Source: "PyTorch
                             FlashAttention-4 adds MXFP8 block-scaled forward and backward
                             for Blackwell", section "Quantization along both axes and
-                            jagged tensors"                                             */
+                            jagged tensors". P is re-quantised to e4m3 per 32 keys
+                            with an E8M0 scale from that block's score maximum        */
+  ATTN_MXFP8_E4M3_PFIX_E4M3 = 3,
+                         /* the same inputs, but P is multiplied by 2^max_offset
+                            (max_offset = 8) and cast to E4M3 with one fixed scale, as
+                            FA4's FP8 path does ("FlashAttention-4's Softmax Tricks",
+                            section "Where 'exact' breaks: P in FP8"); a lagging max
+                            lets P reach 2^tau, so tau < log2(448) - 8 (about 0.807)
+                            is required (ATTN_E_TAU otherwise)                         */
+  ATTN_MXFP8_E4M3_PFIX_E5M2 = 4
+                         /* as ATTN_MXFP8_E4M3_PFIX_E4M3 with P cast to E5M2 (largest
+                            finite 57344): tau < log2(57344) - 8 (about 7.807)          */
 };
 
 /*
@@ -118,16 +131,18 @@ int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
 /*
  * attn_fwd_ex -- attn_fwd with an explicit dtype, MX scales and stream.
  *
- *   dtype     ATTN_F32, ATTN_BF16 or ATTN_MXFP8_E4M3
+ *   dtype     ATTN_F32, ATTN_BF16, ATTN_MXFP8_E4M3, ATTN_MXFP8_E4M3_PFIX_E4M3 or
+ *             ATTN_MXFP8_E4M3_PFIX_E5M2
  *   q_scale, k_scale, v_scale
  *             device uint8 E8M0 bytes, [B,H,Nq/32,d/32] and [B,H,Nk/32,d/32];
- *             required for ATTN_MXFP8_E4M3, ignored (may be NULL) otherwise
+ *             required for the three MXFP8 dtypes, ignored (may be NULL) otherwise
  *   stream    a hipStream_t (e.g. torch.cuda.current_stream().cuda_stream), or NULL
- * For MXFP8, P is re-quantised to e4m3 per 32 keys with an E8M0 scale taken from
- * that block's score maximum, so a lagging max cannot saturate P (the failure
- * "FlashAttention-4's Softmax Tricks" describes in "Where 'exact' breaks: P in
- * FP8" needs a fixed per-tensor P scale); tau = 0, the setting that page gives
- * for FP8, is the usual choice.
+ * For ATTN_MXFP8_E4M3, P is re-quantised to e4m3 per 32 keys with an E8M0 scale
+ * taken from that block's score maximum, so a lagging max cannot saturate P (the
+ * failure "FlashAttention-4's Softmax Tricks" describes in "Where 'exact' breaks:
+ * P in FP8" needs a fixed P scale); tau = 0, the setting that page gives for FP8,
+ * is the usual choice. The two PFIX dtypes use that fixed scale and therefore
+ * bound tau by the P format's range.
  */
 int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
                 int B, int H, int Nq, int Nk, int d, int causal, float scale,

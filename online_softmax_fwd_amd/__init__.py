@@ -10,7 +10,10 @@ missing or cannot be loaded, every call raises.
 q, k, v: contiguous CUDA (HIP) tensors [B, H, N, d], float32 or bfloat16,
 or uint8 e4m3 bytes with ``q_scale``/``k_scale``/``v_scale`` E8M0 bytes
 [B, H, N/32, d/32] for the MXFP8 path. O has q's dtype (bfloat16 for MXFP8);
-LSE is float32 [B, H, Nq], natural log.
+LSE is float32 [B, H, Nq], natural log. For MXFP8, ``fp8_p`` picks how P is
+cast before the PV MFMA: "block" (one E8M0 scale per 32 keys), "e4m3" or
+"e5m2" (P times 2^8 with one fixed scale; tau is then bounded by the
+format's range).
 """
 from __future__ import annotations
 
@@ -19,9 +22,12 @@ import math
 import os
 
 __all__ = ["fwd", "fwd_stats", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
-           "ATTN_F32", "ATTN_BF16", "ATTN_MXFP8_E4M3", "EXP2_MODES", "STATUS"]
+           "ATTN_F32", "ATTN_BF16", "ATTN_MXFP8_E4M3", "ATTN_MXFP8_E4M3_PFIX_E4M3", "ATTN_MXFP8_E4M3_PFIX_E5M2",
+           "EXP2_MODES", "STATUS"]
 
 ATTN_F32, ATTN_BF16, ATTN_MXFP8_E4M3 = 0, 1, 2
+ATTN_MXFP8_E4M3_PFIX_E4M3, ATTN_MXFP8_E4M3_PFIX_E5M2 = 3, 4
+FP8_P = {"block": ATTN_MXFP8_E4M3, "e4m3": ATTN_MXFP8_E4M3_PFIX_E4M3, "e5m2": ATTN_MXFP8_E4M3_PFIX_E5M2}
 EXP2_MODES = {"hw": 0, "emu": 1, "mix": 2}
 MIX_BASE = 16
 STATUS = {0: "ATTN_OK", -1: "ATTN_E_NULLPTR", -2: "ATTN_E_SHAPE", -3: "ATTN_E_HEADDIM", -4: "ATTN_E_DTYPE",
@@ -88,7 +94,7 @@ def _stream_ptr(stream, device):
     return stream.cuda_stream
 
 
-def _prepare(q, k, v, out, lse, q_scale, k_scale, v_scale):
+def _prepare(q, k, v, out, lse, q_scale, k_scale, v_scale, fp8_p="block"):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -102,7 +108,9 @@ def _prepare(q, k, v, out, lse, q_scale, k_scale, v_scale):
     elif q.dtype == torch.bfloat16:
         dtype, odt = ATTN_BF16, torch.bfloat16
     elif q.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
-        dtype, odt = ATTN_MXFP8_E4M3, torch.bfloat16
+        if fp8_p not in FP8_P:
+            raise ValueError(f"fp8_p must be one of {sorted(FP8_P)}")
+        dtype, odt = FP8_P[fp8_p], torch.bfloat16
     else:
         raise ValueError(f"unsupported dtype {q.dtype}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -119,7 +127,7 @@ def _prepare(q, k, v, out, lse, q_scale, k_scale, v_scale):
     if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse has the wrong shape, dtype or layout")
     scales = [0, 0, 0]
-    if dtype == ATTN_MXFP8_E4M3:
+    if dtype in FP8_P.values():
         for i, (name, s, n) in enumerate((("q_scale", q_scale, Nq), ("k_scale", k_scale, k.shape[2]),
                                           ("v_scale", v_scale, k.shape[2]))):
             if s is None or s.dtype != torch.uint8 or not s.is_contiguous() or \
@@ -130,10 +138,10 @@ def _prepare(q, k, v, out, lse, q_scale, k_scale, v_scale):
 
 
 def fwd(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 8.0, out=None, lse=None,
-        q_scale=None, k_scale=None, v_scale=None, stream=None):
+        q_scale=None, k_scale=None, v_scale=None, stream=None, fp8_p="block"):
     """Attention forward through attn_fwd_ex. Returns (O, LSE); asynchronous on `stream`."""
     lib = load_library()
-    dtype, out, lse, scales = _prepare(q, k, v, out, lse, q_scale, k_scale, v_scale)
+    dtype, out, lse, scales = _prepare(q, k, v, out, lse, q_scale, k_scale, v_scale, fp8_p)
     B, H, Nq, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _check(lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -143,11 +151,11 @@ def fwd(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 
 
 
 def fwd_stats(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 8.0,
-              q_scale=None, k_scale=None, v_scale=None, stream=None):
+              q_scale=None, k_scale=None, v_scale=None, stream=None, fp8_p="block"):
     """fwd plus the rescale counters: returns (O, LSE, stats[4] uint64 on the host)."""
     import torch
     lib = load_library()
-    dtype, out, lse, scales = _prepare(q, k, v, None, None, q_scale, k_scale, v_scale)
+    dtype, out, lse, scales = _prepare(q, k, v, None, None, q_scale, k_scale, v_scale, fp8_p)
     B, H, Nq, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = torch.zeros(4, dtype=torch.int64, device=q.device)

@@ -26,6 +26,11 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool is_mx(int dtype) {
+  return dtype == ATTN_MXFP8_E4M3 || dtype == ATTN_MXFP8_E4M3_PFIX_E4M3 || dtype == ATTN_MXFP8_E4M3_PFIX_E5M2;
+}
+constexpr int kPMaxOffset = 8;  // P scale exponent of the fixed-scale FP8 P dtypes
+
 // Emulated share of P (16ths) for ATTN_EXP2_MIX, keyed by (dtype, d, causal).
 // The first page reports the Blackwell kernel's shares ("FlashAttention-4's
 // Softmax Tricks", section "The emulated exp2": 18.75 % non-causal d=128,
@@ -46,6 +51,8 @@ int mix_table(int dtype, int d, int causal) {
     case ATTN_F32:
       return 0;
     case ATTN_MXFP8_E4M3:
+    case ATTN_MXFP8_E4M3_PFIX_E4M3:
+    case ATTN_MXFP8_E4M3_PFIX_E5M2:
       return causal ? 0 : 1;
     default:
       return -1;
@@ -56,8 +63,8 @@ int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void
                       int B, int H, int Nq, int Nk, int d, int causal, float scale, int exp2_mode, float tau,
                       int dtype, const uint8_t* qs, const uint8_t* ks, const uint8_t* vs, bool* nothing) {
   *nothing = false;
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_MXFP8_E4M3)
-    return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32, ATTN_BF16 or ATTN_MXFP8_E4M3", dtype);
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && !is_mx(dtype))
+    return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32, ATTN_BF16 or one of the ATTN_MXFP8 codes", dtype);
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
     return fail(ATTN_E_SHAPE, "negative size (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
   if (d != 64 && d != 128) return fail(ATTN_E_HEADDIM, "head dim d=%d is not 64 or 128", d);
@@ -67,6 +74,14 @@ int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void
                 (double)scale);
   if (!std::isfinite(tau) || tau < 0.0f || tau > 64.0f)
     return fail(ATTN_E_TAU, "tau=%g must be finite and in [0, 64]", (double)tau);
+  // A fixed P scale of 2^max_offset lets a lagging max push P up to
+  // 2^(max_offset + tau), which must stay below the format's largest value.
+  if (dtype == ATTN_MXFP8_E4M3_PFIX_E4M3 || dtype == ATTN_MXFP8_E4M3_PFIX_E5M2) {
+    const double pmax = dtype == ATTN_MXFP8_E4M3_PFIX_E4M3 ? 448.0 : 57344.0;
+    if (!(kPMaxOffset + (double)tau < std::log2(pmax)))
+      return fail(ATTN_E_TAU, "tau=%g: with P scaled by 2^%d, max_offset + tau must stay below log2(%g) = %.3f",
+                  (double)tau, kPMaxOffset, pmax, std::log2(pmax));
+  }
   int emu16;
   if (exp2_mode == ATTN_EXP2_HW) {
     emu16 = 0;
@@ -95,16 +110,17 @@ int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void
   // The kernels address one (batch, head) slice of Q, K or V through a buffer
   // resource with 32-bit byte offsets, up to one key tile past the end.
   const long long esize = dtype == ATTN_F32 ? 4 : dtype == ATTN_BF16 ? 2 : 1;
+  const bool mx = is_mx(dtype);
   if (((long long)std::max(Nq, Nk) + 256) * d * esize > 0x7FFFFFFFLL)
     return fail(ATTN_E_SHAPE, "one (batch, head) slice of Q, K or V must stay under 2 GiB (Nq=%d Nk=%d d=%d)", Nq,
                 Nk, d);
-  if (dtype == ATTN_MXFP8_E4M3 && (Nq % 32 != 0 || Nk % 32 != 0))
+  if (mx && (Nq % 32 != 0 || Nk % 32 != 0))
     return fail(ATTN_E_SHAPE, "MXFP8 needs Nq and Nk to be multiples of 32 (Nq=%d Nk=%d)", Nq, Nk);
   if (!Q || !K || !V || !O || !LSE) return fail(ATTN_E_NULLPTR, "Q, K, V, O and LSE must be non-NULL");
-  if (dtype == ATTN_MXFP8_E4M3 && (!qs || !ks || !vs))
+  if (mx && (!qs || !ks || !vs))
     return fail(ATTN_E_NULLPTR, "MXFP8 needs q_scale, k_scale and v_scale");
-  if (dtype == ATTN_MXFP8_E4M3 && d != 128) return fail(ATTN_E_HEADDIM, "MXFP8 supports d=128 (got %d)", d);
-  if (dtype == ATTN_MXFP8_E4M3 &&
+  if (mx && d != 128) return fail(ATTN_E_HEADDIM, "MXFP8 supports d=128 (got %d)", d);
+  if (mx &&
       ((reinterpret_cast<uintptr_t>(qs) | reinterpret_cast<uintptr_t>(ks) | reinterpret_cast<uintptr_t>(vs)) & 3u))
     return fail(ATTN_E_ALIGN, "MX scale pointers must be 4-byte aligned");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
@@ -137,7 +153,7 @@ int run(const attn::FwdArgs& a, int dtype, void* stream) {
   switch (dtype) {
     case ATTN_BF16: e = attn::launch_fwd_bf16(a, s); break;
     case ATTN_F32: e = attn::launch_fwd_f32(a, s); break;
-    default: e = attn::launch_fwd_mxfp8(a, s); break;
+    default: e = attn::launch_fwd_mxfp8(a, dtype - ATTN_MXFP8_E4M3, s); break;
   }
   if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;

@@ -114,7 +114,16 @@ __device__ __forceinline__ uint32_t e8m0_of(float amax) {
 }
 __device__ __forceinline__ float inv_scale(uint32_t byte) { return __builtin_bit_cast(float, (254u - byte) << 23); }
 
-template <bool CAUSAL, int EMU16>
+// P quantisation: kPBlock = one E8M0 scale per 32-key block from the block
+// amax (the MXFP8 page's design); kPFixedE4M3 / kPFixedE5M2 = P times the
+// fixed 2^max_offset with max_offset = 8 and one constant scale byte, cast to
+// E4M3 or E5M2 ("FlashAttention-4's Softmax Tricks", section "Where 'exact'
+// breaks: P in FP8"); the boundary only admits tau with
+// max_offset + tau < log2(largest finite value), so the cast never saturates.
+enum { kPBlock = 0, kPFixedE4M3 = 1, kPFixedE5M2 = 2 };
+constexpr int kMaxOffset = 8;
+
+template <bool CAUSAL, int EMU16, int PMODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
                       const uint8_t* __restrict__ QS, const uint8_t* __restrict__ KS, const uint8_t* __restrict__ VS,
@@ -282,21 +291,34 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
     l_run = __builtin_fmaf(l_run, alpha, sum16(s[0]) + sum16(s[1]));
 
     // P -> e4m3 per 32-key block; the block amax from the reused block max
-    const uint32_t sb0 = e8m0_of(exp2_hw(__builtin_fmaf(bm0, c, -mc)));
-    const uint32_t sb1 = e8m0_of(exp2_hw(__builtin_fmaf(bm1, c, -mc)));
+    uint32_t sb0, sb1;
+    if constexpr (PMODE == kPBlock) {
+      sb0 = e8m0_of(exp2_hw(__builtin_fmaf(bm0, c, -mc)));
+      sb1 = e8m0_of(exp2_hw(__builtin_fmaf(bm1, c, -mc)));
+    } else {
+      sb0 = sb1 = 127 - kMaxOffset;  // P is stored times 2^max_offset
+    }
     const float inv0 = inv_scale(sb0), inv1 = inv_scale(sb1);
     i32x8 pq;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       int lo = 0, hi = 0;
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * w] * inv0, s[0][4 * w + 1] * inv0, lo, false);
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * w + 2] * inv0, s[0][4 * w + 3] * inv0, lo, true);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * w] * inv1, s[1][4 * w + 1] * inv1, hi, false);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * w + 2] * inv1, s[1][4 * w + 3] * inv1, hi, true);
+      if constexpr (PMODE == kPFixedE5M2) {
+        lo = __builtin_amdgcn_cvt_pk_bf8_f32(s[0][4 * w] * inv0, s[0][4 * w + 1] * inv0, lo, false);
+        lo = __builtin_amdgcn_cvt_pk_bf8_f32(s[0][4 * w + 2] * inv0, s[0][4 * w + 3] * inv0, lo, true);
+        hi = __builtin_amdgcn_cvt_pk_bf8_f32(s[1][4 * w] * inv1, s[1][4 * w + 1] * inv1, hi, false);
+        hi = __builtin_amdgcn_cvt_pk_bf8_f32(s[1][4 * w + 2] * inv1, s[1][4 * w + 3] * inv1, hi, true);
+      } else {
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * w] * inv0, s[0][4 * w + 1] * inv0, lo, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * w + 2] * inv0, s[0][4 * w + 3] * inv0, lo, true);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * w] * inv1, s[1][4 * w + 1] * inv1, hi, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * w + 2] * inv1, s[1][4 * w + 3] * inv1, hi, true);
+      }
       pq[w] = lo;
       pq[4 + w] = hi;
     }
     const int pscale = (int)(hh ? sb1 : sb0);
+    constexpr int kPFmt = PMODE == kPFixedE5M2 ? 1 : 0;  // MFMA B-operand format: 0 = E4M3, 1 = E5M2
 
     // O^T += V^T P^T
 #pragma unroll
@@ -310,10 +332,10 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
         a[2 * r + 1] = v[1];
       }
       switch (db) {
-        case 0: o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[0], 0, 0, 0, vscale, 0, pscale); break;
-        case 1: o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[1], 0, 0, 1, vscale, 0, pscale); break;
-        case 2: o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[2], 0, 0, 2, vscale, 0, pscale); break;
-        default: o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[3], 0, 0, 3, vscale, 0, pscale); break;
+        case 0: o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[0], 0, kPFmt, 0, vscale, 0, pscale); break;
+        case 1: o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[1], 0, kPFmt, 1, vscale, 0, pscale); break;
+        case 2: o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[2], 0, kPFmt, 2, vscale, 0, pscale); break;
+        default: o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pq, o[3], 0, kPFmt, 3, vscale, 0, pscale); break;
       }
     }
   };
@@ -354,35 +376,45 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   }
 }
 
-template <bool CAUSAL, int EMU16>
+template <bool CAUSAL, int EMU16, int PMODE>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
   const long long grid = (long long)a.B * a.H * n_qt;
-  hipLaunchKernelGGL((fwd_mxfp8_kernel<CAUSAL, EMU16>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fwd_mxfp8_kernel<CAUSAL, EMU16, PMODE>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_scale, a.k_scale, a.v_scale,
                      (__bf16*)a.o, a.lse, a.stats, a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau);
   return hipGetLastError();
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, int PMODE>
 hipError_t launch_mode(const FwdArgs& a, hipStream_t stream) {
   switch (a.emu16) {
-    case 0: return launch<CAUSAL, 0>(a, stream);
-    case 1: return launch<CAUSAL, 1>(a, stream);
-    case 2: return launch<CAUSAL, 2>(a, stream);
-    case 3: return launch<CAUSAL, 3>(a, stream);
-    case 4: return launch<CAUSAL, 4>(a, stream);
-    case 8: return launch<CAUSAL, 8>(a, stream);
-    case 16: return launch<CAUSAL, 16>(a, stream);
+    case 0: return launch<CAUSAL, 0, PMODE>(a, stream);
+    case 1: return launch<CAUSAL, 1, PMODE>(a, stream);
+    case 2: return launch<CAUSAL, 2, PMODE>(a, stream);
+    case 3: return launch<CAUSAL, 3, PMODE>(a, stream);
+    case 4: return launch<CAUSAL, 4, PMODE>(a, stream);
+    case 8: return launch<CAUSAL, 8, PMODE>(a, stream);
+    case 16: return launch<CAUSAL, 16, PMODE>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int PMODE>
+hipError_t launch_p(const FwdArgs& a, hipStream_t stream) {
+  return a.causal ? launch_mode<true, PMODE>(a, stream) : launch_mode<false, PMODE>(a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_fwd_mxfp8(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_fwd_mxfp8(const FwdArgs& a, int p_mode, hipStream_t stream) {
   if (a.d != kD) return hipErrorInvalidValue;
-  return a.causal ? launch_mode<true>(a, stream) : launch_mode<false>(a, stream);
+  switch (p_mode) {
+    case kPBlock: return launch_p<kPBlock>(a, stream);
+    case kPFixedE4M3: return launch_p<kPFixedE4M3>(a, stream);
+    case kPFixedE5M2: return launch_p<kPFixedE5M2>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace attn

@@ -27,7 +27,9 @@ struct FwdArgs {
 // Each returns hipSuccess or the launch error; none synchronises.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_fwd_mxfp8(const FwdArgs& a, hipStream_t stream);
+// p_mode: 0 = P scaled per 32-key block, 1 = fixed 2^8 scale with E4M3 P,
+// 2 = fixed 2^8 scale with E5M2 P
+hipError_t launch_fwd_mxfp8(const FwdArgs& a, int p_mode, hipStream_t stream);
 hipError_t launch_exp2(const float* x, float* y, long n, int emulated, hipStream_t stream);
 
 // Emulated shares (in 16ths) that have a compiled kernel instance.

@@ -72,6 +72,13 @@ def _call(lib, **kw):
     (dict(dtype=2, Nq=100), -2),      # MXFP8 needs multiples of 32
     (dict(dtype=2), -1),              # MXFP8 needs scales
     (dict(Nq=1 << 31 - 1, B=1 << 20), -2),
+    (dict(dtype=5), -4),
+    (dict(dtype=3, tau=0.81), -6),    # E4M3 P times 2^8: 8 + tau must stay below log2(448) = 8.807
+    (dict(dtype=3, tau=8.0), -6),
+    (dict(dtype=4, tau=7.81), -6),    # E5M2 P: below log2(57344) = 15.807
+    (dict(dtype=3, tau=0.5), -1),     # tau accepted; fails later on the missing MX scales
+    (dict(dtype=4, tau=7.5), -1),
+    (dict(dtype=3, tau=0.0, d=64), -1),
     (dict(Nk=1 << 23), -2),           # one bf16 d=128 K/V slice of 2 GiB or more
     (dict(Nq=1 << 24, d=64, dtype=0), -2),  # f32 Q slice of 4 GiB
 ])
@@ -106,7 +113,7 @@ def test_stats_validation(lib):
 
 
 def test_mix_table(lib):
-    for dtype in (0, 1, 2):
+    for dtype in (0, 1, 2, 3, 4):
         for d in (64, 128):
             for causal in (0, 1):
                 k = lib.attn_mix_sixteenths(dtype, d, causal)
