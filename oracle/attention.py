@@ -39,22 +39,44 @@ def _default_scale(d: int, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def _one_head(q, k, v, causal, scale, rows):
-    """Plain definition for one head. q: [R, d] at global query indices `rows`."""
+def causal_offset(causal, nq: int, nk: int):
+    """None for no mask, else the offset c of the mask "key j is hidden from
+    query i when j > i + c". True or "top_left": c = 0, the lecture's
+    S_ij = -inf for j > i. "bottom_right": c = Nk - Nq, so the last query sees
+    every key (the same mask when Nq = Nk)."""
+    if causal is False or causal is None:
+        return None
+    if causal is True or causal == "top_left":
+        return 0
+    if causal == "bottom_right":
+        return nk - nq
+    raise ValueError(f"causal={causal!r}")
+
+
+def _one_head(q, k, v, causal, scale, rows, nq):
+    """Plain definition for one head. q: [R, d] at global query indices `rows`
+    of nq. A row that sees no key (possible bottom-right with Nq > Nk) has no
+    softmax; it gets O = 0 and LSE = -inf."""
     s = scale * (q @ k.T)                                   # [R, Nk]
-    if causal:
+    off = causal_offset(causal, nq, k.shape[0])
+    if off is not None:
         cols = np.arange(k.shape[0])
-        s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
+        s = np.where(cols[None, :] > rows[:, None] + off, -np.inf, s)
     m = s.max(axis=1)
+    empty = ~np.isfinite(m)
+    m = np.where(empty, 0.0, m)
     e = np.exp(s - m[:, None])
     den = e.sum(axis=1)
-    o = (e @ v) / den[:, None]
-    lse = m + np.log(den)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = np.where(empty[:, None], 0.0, (e @ v) / den[:, None])
+        lse = np.where(empty, -np.inf, m + np.log(den))
     return o, lse
 
 
-def attention_f64(q, k, v, causal: bool = False, scale=None, chunk: int = 256):
+def attention_f64(q, k, v, causal=False, scale=None, chunk: int = 256):
     """O [B, H, Nq, dv] float64 and LSE [B, H, Nq] float64.
+
+    causal: False, True / "top_left", or "bottom_right" (see causal_offset).
 
     q: [B, H, Nq, d], k: [B, H, Nk, d], v: [B, H, Nk, dv]; any real dtype.
     Query rows are processed in chunks only to bound memory; every row is a
@@ -72,7 +94,7 @@ def attention_f64(q, k, v, causal: bool = False, scale=None, chunk: int = 256):
             for r0 in range(0, Nq, chunk):
                 rows = np.arange(r0, min(Nq, r0 + chunk))
                 o[b, h, rows], lse[b, h, rows] = _one_head(q[b, h, rows], k[b, h], v[b, h],
-                                                           causal, scale, rows)
+                                                           causal, scale, rows, Nq)
     return o, lse
 
 
@@ -83,7 +105,7 @@ def attention_rows_f64(q, k, v, b: int, h: int, rows, causal: bool = False, scal
     qq = np.asarray(q[b, h, rows], dtype=np.float64)
     kk = np.asarray(k[b, h], dtype=np.float64)
     vv = np.asarray(v[b, h], dtype=np.float64)
-    return _one_head(qq, kk, vv, causal, _default_scale(d, scale), rows)
+    return _one_head(qq, kk, vv, causal, _default_scale(d, scale), rows, q.shape[2])
 
 
 def blockwise_f64(q, k, v, causal: bool = False, scale=None, block: int = 64,
@@ -130,6 +152,7 @@ def blockwise_f64(q, k, v, causal: bool = False, scale=None, block: int = 64,
         dv = vv_all.shape[-1]
         scale_log2 = _default_scale(d, scale) * _LOG2E
     nblk = -(-Nk // block)
+    off = causal_offset(causal, Nq, Nk)
     o_out = np.empty((B, H, Nq, dv))
     lse_out = np.empty((B, H, Nq))
     events = np.zeros((B, H, Nq, nblk), dtype=bool)
@@ -145,9 +168,9 @@ def blockwise_f64(q, k, v, causal: bool = False, scale=None, block: int = 64,
                     s = s2_all[b, h, :, k0:k1]
                 else:
                     s = q[b, h] @ k[b, h, k0:k1].T              # raw units
-                if causal:
+                if off is not None:
                     cols = np.arange(k0, k1)
-                    s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
+                    s = np.where(cols[None, :] > rows[:, None] + off, -np.inf, s)
                 seen = np.isfinite(s).any(axis=1)
                 m_new = np.maximum(row_max, s.max(axis=1))
                 with np.errstate(invalid="ignore"):
@@ -163,8 +186,10 @@ def blockwise_f64(q, k, v, causal: bool = False, scale=None, block: int = 64,
                 acc_o = acc_o * factor[:, None] + p @ vv_all[b, h, k0:k1]
                 row_max = m_use
             with np.errstate(divide="ignore", invalid="ignore"):
-                o_out[b, h] = acc_o / row_sum[:, None]
-                lse_out[b, h] = math.log(2.0) * (row_max * scale_log2 + np.log2(row_sum))
+                empty = row_sum == 0                 # rows that saw no key
+                o_out[b, h] = np.where(empty[:, None], 0.0, acc_o / row_sum[:, None])
+                lse_out[b, h] = np.where(empty, -np.inf,
+                                         math.log(2.0) * (row_max * scale_log2 + np.log2(row_sum)))
     ev = events.reshape(B * H * Nq, nblk)
     ng = (B * H * Nq) // group
     groups = ev[: ng * group].reshape(ng, group, nblk).any(axis=1)

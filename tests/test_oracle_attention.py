@@ -205,3 +205,57 @@ def test_rescale_frequency_table(golden_dir):
             # sampling noise: about 0.2 points on rows, 3 points on warps
             assert abs(rows_pct - exp_rows) <= max(0.6, 0.03 * exp_rows), (row["scores"], tau, rows_pct)
             assert abs(warps_pct - exp_warps) <= 5.0, (row["scores"], tau, warps_pct)
+
+
+# --- causal alignment when Nq != Nk ------------------------------------------
+@pytest.mark.parametrize("nq,nk", [(37, 37), (11, 37), (37, 11), (1, 20), (20, 1)])
+def test_bottom_right_equal_scores(nq, nk):
+    # Q = 0: row i sees keys 0 .. i + Nk - Nq (bottom-right alignment), so O_i is
+    # their mean and LSE_i = ln(count); a row that sees none gets O = 0, LSE = -inf
+    q = np.zeros((1, 2, nq, 8))
+    k = _rand((1, 2, nk, 8), 3)
+    v = _rand((1, 2, nk, 5), 4)
+    o, lse = attention_f64(q, k, v, causal="bottom_right", scale=0.9)
+    for i in range(nq):
+        n = min(nk, max(0, i + nk - nq + 1))
+        if n == 0:
+            assert np.all(o[:, :, i] == 0.0) and np.all(lse[:, :, i] == -np.inf)
+        else:
+            np.testing.assert_allclose(o[:, :, i], v[:, :, :n].mean(axis=2), rtol=0, atol=1e-14)
+            np.testing.assert_allclose(lse[:, :, i], math.log(n), rtol=0, atol=1e-14)
+
+
+def test_bottom_right_equals_top_left_when_square_and_last_row_sees_all():
+    q, k, v = _rand((2, 2, 24, 16), 5), _rand((2, 2, 24, 16), 6), _rand((2, 2, 24, 16), 7)
+    o1, l1 = attention_f64(q, k, v, causal=True)
+    o2, l2 = attention_f64(q, k, v, causal="bottom_right")
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    q = _rand((1, 2, 9, 16), 8)
+    k, v = _rand((1, 2, 30, 16), 9), _rand((1, 2, 30, 16), 10)
+    on, ln_ = attention_f64(q, k, v, causal=False)
+    ob, lb = attention_f64(q, k, v, causal="bottom_right")
+    np.testing.assert_allclose(ob[:, :, -1], on[:, :, -1], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lb[:, :, -1], ln_[:, :, -1], rtol=0, atol=1e-14)
+    # and the top-left mask keeps the first row to key 0 only
+    ot, _ = attention_f64(q, k, v, causal=True)
+    np.testing.assert_allclose(ot[:, :, 0], v[:, :, 0], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("nq,nk", [(13, 40), (40, 13)])
+def test_bottom_right_brute_force_and_blockwise(nq, nk):
+    q, k, v = _rand((1, 1, nq, 6), 11), _rand((1, 1, nk, 6), 12), _rand((1, 1, nk, 3), 13)
+    o, lse = attention_f64(q, k, v, causal="bottom_right", scale=0.5)
+    for i in range(nq):
+        keys = [j for j in range(nk) if j <= i + nk - nq]
+        if not keys:
+            continue
+        sc = [0.5 * float(np.dot(q[0, 0, i], k[0, 0, j])) for j in keys]
+        np.testing.assert_allclose(lse[0, 0, i], scipy.special.logsumexp(sc), rtol=0, atol=1e-13)
+        w = scipy.special.softmax(sc)
+        np.testing.assert_allclose(o[0, 0, i], w @ v[0, 0, keys], rtol=0, atol=1e-13)
+    for tau in (0.0, 8.0):
+        ob, lb, _ = blockwise_f64(q, k, v, causal="bottom_right", scale=0.5, block=8, tau=tau)
+        fin = np.isfinite(lse)
+        np.testing.assert_allclose(ob, o, rtol=0, atol=1e-12)
+        assert np.array_equal(np.isfinite(lb), fin)
+        np.testing.assert_allclose(lb[fin], lse[fin], rtol=0, atol=1e-12)
