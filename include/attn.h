@@ -115,7 +115,13 @@ enum {
  *   B, H, Nq  >= 0 (a zero means there is nothing to do: returns ATTN_OK)
  *   Nk        >= 1 when B*H*Nq > 0
  *   d         64 or 128
- *   causal    0 or 1 (top-left aligned mask, key j > query i removed)
+ *   causal    0 = no mask; 1 = causal aligned top-left: key j is removed for
+ *             query i when j > i ("Lecture 2 -- Online Softmax and Numerical
+ *             Correctness", section "Causal masking just changes which blocks
+ *             contribute"); 2 = causal aligned bottom-right: removed when
+ *             j > i + Nk - Nq, so the last query sees every key (the same mask as
+ *             1 when Nq == Nk). A row that sees no key (2 with Nq > Nk) gets
+ *             O = 0 and LSE = -inf.
  *   scale     > 0 and finite; multiplies Q.K (1/sqrt(d) for standard attention)
  *   exp2_mode ATTN_EXP2_* above
  *   tau       lagging-max threshold in log2 units of the scaled scores

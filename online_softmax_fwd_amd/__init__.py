@@ -87,6 +87,18 @@ def _mode(exp2_mode) -> int:
     return EXP2_MODES[exp2_mode]
 
 
+def _causal(causal) -> int:
+    """False/0: no mask; True/1/"top_left": key j > query i removed;
+    2/"bottom_right": key j > i + Nk - Nq removed."""
+    if causal in ("top_left",):
+        return 1
+    if causal in ("bottom_right",):
+        return 2
+    if isinstance(causal, (bool, int)) and int(causal) in (0, 1, 2):
+        return int(causal)
+    raise ValueError(f"causal={causal!r}: use False, True / 'top_left' or 'bottom_right'")
+
+
 def _stream_ptr(stream, device):
     import torch
     if stream is None:
@@ -145,7 +157,7 @@ def fwd(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 
     B, H, Nq, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _check(lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                           B, H, Nq, k.shape[2], d, int(bool(causal)), scale, _mode(exp2_mode), float(tau),
+                           B, H, Nq, k.shape[2], d, _causal(causal), scale, _mode(exp2_mode), float(tau),
                            dtype, scales[0], scales[1], scales[2], _stream_ptr(stream, q.device)))
     return out, lse
 
@@ -160,7 +172,7 @@ def fwd_stats(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: fl
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = torch.zeros(4, dtype=torch.int64, device=q.device)
     _check(lib.attn_fwd_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                              B, H, Nq, k.shape[2], d, int(bool(causal)), scale, _mode(exp2_mode), float(tau),
+                              B, H, Nq, k.shape[2], d, _causal(causal), scale, _mode(exp2_mode), float(tau),
                               dtype, scales[0], scales[1], scales[2], st.data_ptr(),
                               _stream_ptr(stream, q.device)))
     return out, lse, st.cpu().tolist()

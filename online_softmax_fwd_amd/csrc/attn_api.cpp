@@ -68,7 +68,8 @@ int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
     return fail(ATTN_E_SHAPE, "negative size (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
   if (d != 64 && d != 128) return fail(ATTN_E_HEADDIM, "head dim d=%d is not 64 or 128", d);
-  if (causal != 0 && causal != 1) return fail(ATTN_E_SHAPE, "causal=%d is not 0 or 1", causal);
+  if (causal < 0 || causal > 2)
+    return fail(ATTN_E_SHAPE, "causal=%d is not 0 (none), 1 (top-left) or 2 (bottom-right)", causal);
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return fail(ATTN_E_SCALE, "scale=%g must be finite and > 0 (the row max is kept in raw score units)",
                 (double)scale);
@@ -88,7 +89,7 @@ int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void
   } else if (exp2_mode == ATTN_EXP2_EMU) {
     emu16 = 16;
   } else if (exp2_mode == ATTN_EXP2_MIX) {
-    emu16 = mix_table(dtype, d, causal);
+    emu16 = mix_table(dtype, d, causal != 0);
   } else if (exp2_mode >= ATTN_EXP2_MIX_BASE && exp2_mode <= ATTN_EXP2_MIX_BASE + 16) {
     emu16 = exp2_mode - ATTN_EXP2_MIX_BASE;
   } else {
@@ -140,7 +141,8 @@ int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void
   a.Nq = Nq;
   a.Nk = Nk;
   a.d = d;
-  a.causal = causal;
+  a.causal = causal != 0;
+  a.diag = causal == 2 ? Nk - Nq : 0;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
   a.tau = tau;
   a.emu16 = emu16;

@@ -228,7 +228,7 @@ template <int D, bool CAUSAL, int EMU16>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                      __bf16* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats,
-                     int H, int Nq, int Nk, int n_qt, float c, float tau) {
+                     int H, int Nq, int Nk, int n_qt, float c, float tau, int diag) {
   using C = Cfg<D, 64, 8>;
   constexpr int BN = C::BN, KB = C::KB;
   __shared__ __attribute__((aligned(1024))) char kb0[C::TILE];
@@ -293,8 +293,21 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   }
 
-  const int kend = CAUSAL ? min(Nk, q0 + C::BM) : Nk;
+  // causal: key j is hidden from query i when j > i + diag (diag = 0 aligns the
+  // mask top-left, Nk - Nq bottom-right)
+  const int kend = CAUSAL ? min(Nk, q0 + C::BM + diag) : Nk;
   const int T = (kend + BN - 1) / BN;
+  if (T <= 0) {  // no row of this workgroup sees a key (bottom-right, Nq > Nk)
+    if (qi < Nq) {
+      __bf16* op = O + qbase + (size_t)qi * D + 4 * hh;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *(bf16x4*)(op + 32 * db + 8 * g) = bf16x4{};
+      if (hh == 0) LSE[(size_t)bh * Nq + qi] = kNegInf;
+    }
+    return;
+  }
 
   floatx16 o[D / 32];
 #pragma unroll
@@ -326,13 +339,13 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // VALU phase j: softmax of tile j
   auto valu_phase = [&](int j) __attribute__((always_inline)) {
     const int k0 = j * BN;
-    if ((CAUSAL && k0 + BN - 1 > qw0) || (k0 + BN > Nk)) {
+    if ((CAUSAL && k0 + BN - 1 > qw0 + diag) || (k0 + BN > Nk)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = k0 + kb * 32 + 16 * (e >> 3) + 8 * hh + (e & 7);
-          if (key >= Nk || (CAUSAL && key > qi)) s[kb][e] = kNegInf;
+          if (key >= Nk || (CAUSAL && key > qi + diag)) s[kb][e] = kNegInf;
         }
     }
     const float mx = pl_max_halves(tree_max<KB>(s));
@@ -417,7 +430,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // ---- epilogue: O / l, LSE -------------------------------------------------
   const float l_tot = pl_sum_halves(l_run);
-  const float inv = 1.0f / l_tot;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that saw no key: O = 0, LSE = -inf
   if (qi < Nq) {
     __bf16* op = O + qbase + (size_t)qi * D + 4 * hh;
 #pragma unroll
@@ -444,7 +457,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const long long grid = (long long)a.B * a.H * n_qt;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EMU16>), dim3((unsigned)grid), dim3(512), 0, stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.stats, a.H,
-                     a.Nq, a.Nk, n_qt, a.scale_log2, a.tau);
+                     a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.diag);
   return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ template <int D, bool CAUSAL, int EMU16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
 void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                     float* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats,
-                    int H, int Nq, int Nk, int n_qt, float c, float tau) {
+                    int H, int Nq, int Nk, int n_qt, float c, float tau, int diag) {
   using G = GeoF<D>;
   __shared__ __attribute__((aligned(16))) float smem[2 * G::bufElems];
 
@@ -72,7 +72,8 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
     }
   }
 
-  const int kend = CAUSAL ? min(Nk, q0 + kBM) : Nk;
+  // causal: key j is hidden from query i when j > i + diag
+  const int kend = CAUSAL ? min(Nk, q0 + kBM + diag) : Nk;
   const int n_kt = (kend + kBN - 1) / kBN;
 
   floatx4 kreg[G::chunks], vreg[G::chunks];
@@ -115,7 +116,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
     const int buf = t & 1;
     if (t + 1 < n_kt) load_tile(t + 1);
     const int k0 = t * kBN;
-    const bool active = !CAUSAL || k0 <= qw0 + kQW - 1;
+    const bool active = !CAUSAL || k0 <= qw0 + kQW - 1 + diag;
     if (active) {
       const float* ks = smem + buf * G::bufElems;
       const float* vs = ks + G::tileElems;
@@ -132,14 +133,14 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
             s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[st + e], s[kb], 0, 0, 0);
         }
       }
-      const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw0) || (k0 + kBN > Nk);
+      const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw0 + diag) || (k0 + kBN > Nk);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int key = k0 + kb * 32 + 16 * (j >> 3) + 8 * hh + (j & 7);
-            if (key >= Nk || (CAUSAL && key > qi)) s[kb][j] = kNegInf;
+            if (key >= Nk || (CAUSAL && key > qi + diag)) s[kb][j] = kNegInf;
           }
       }
       float mx = kNegInf;
@@ -194,7 +195,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
   }
 
   const float l_tot = sum_halves(l_run);
-  const float inv = 1.0f / l_tot;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that saw no key: O = 0, LSE = -inf
   if (qi < Nq) {
     float* op = O + qbase + (size_t)qi * D + 4 * hh;
 #pragma unroll
@@ -220,7 +221,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const long long grid = (long long)a.B * a.H * n_qt;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, EMU16>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.stats,
-                     a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau);
+                     a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.diag);
   return hipGetLastError();
 }
 

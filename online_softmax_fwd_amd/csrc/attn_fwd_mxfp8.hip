@@ -128,7 +128,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
                       const uint8_t* __restrict__ QS, const uint8_t* __restrict__ KS, const uint8_t* __restrict__ VS,
                       __bf16* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats, int H,
-                      int Nq, int Nk, int n_qt, float c, float tau) {
+                      int Nq, int Nk, int n_qt, float c, float tau, int diag) {
   __shared__ __attribute__((aligned(1024))) char kb0[kTile];
   __shared__ __attribute__((aligned(1024))) char kb1[kTile];
   __shared__ __attribute__((aligned(1024))) char vb0[kTile];
@@ -200,7 +200,8 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   // byte 2s of (qsc >> 8h) is the scale of d block 2s + h: op_sel picks byte 2s
   const int qscale = (int)(qsc >> (8 * hh));
 
-  const int kend = CAUSAL ? min(Nk, q0 + kBM) : Nk;
+  // causal: key j is hidden from query i when j > i + diag
+  const int kend = CAUSAL ? min(Nk, q0 + kBM + diag) : Nk;
   const int n_kt = (kend + kBN - 1) / kBN;
 
   floatx16 o[4];
@@ -224,7 +225,7 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
 
   auto compute = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
     const int k0 = t * kBN;
-    if ((CAUSAL && k0 > qw0 + 31) || !wave_rows) return;  // wave-uniform: nothing to add
+    if ((CAUSAL && k0 > qw0 + 31 + diag) || !wave_rows) return;  // wave-uniform: nothing to add
     const uint8_t* ksb = KS + (size_t)bh * nkb * 4;
     const uint8_t* vsb = VS + (size_t)bh * nkb * 4;
     const uint32_t kw0 = scale_word(ksb, 2 * t, nkb), kw1 = scale_word(ksb, 2 * t + 1, nkb);
@@ -250,13 +251,13 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
       }
     }
 
-    if ((CAUSAL && k0 + kBN - 1 > qw0) || (k0 + kBN > Nk)) {
+    if ((CAUSAL && k0 + kBN - 1 > qw0 + diag) || (k0 + kBN > Nk)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = k0 + 32 * kb + 16 * hh + e;
-          if (key >= Nk || (CAUSAL && key > qi)) s[kb][e] = kNegInf;
+          if (key >= Nk || (CAUSAL && key > qi + diag)) s[kb][e] = kNegInf;
         }
     }
 
@@ -356,7 +357,7 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   }
 
   const float l_tot = pl_sum_halves(l_run);
-  const float inv = 1.0f / l_tot;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that saw no key: O = 0, LSE = -inf
   if (wave_rows) {
     __bf16* op = O + qbase + (size_t)qi * kD + 4 * hh;
 #pragma unroll
@@ -382,7 +383,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const long long grid = (long long)a.B * a.H * n_qt;
   hipLaunchKernelGGL((fwd_mxfp8_kernel<CAUSAL, EMU16, PMODE>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_scale, a.k_scale, a.v_scale,
-                     (__bf16*)a.o, a.lse, a.stats, a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau);
+                     (__bf16*)a.o, a.lse, a.stats, a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.diag);
   return hipGetLastError();
 }
 

@@ -18,7 +18,8 @@ struct FwdArgs {
   const uint8_t* v_scale;
   unsigned long long* stats;  // optional rescale counters (4 x uint64)
   int B, H, Nq, Nk, d;
-  int causal;
+  int causal;               // 0 or 1
+  int diag;                 // causal: key j hidden from query i when j > i + diag
   float scale_log2;         // scale * log2(e)
   float tau;                // lagging-max threshold, log2 units
   int emu16;                // software-exp2 share of P, in 16ths (0 = all hardware)

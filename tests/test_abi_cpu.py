@@ -55,7 +55,8 @@ def _call(lib, **kw):
     (dict(Nk=0), -2),
     (dict(d=96), -3),
     (dict(d=256), -3),
-    (dict(causal=2), -2),
+    (dict(causal=3), -2),
+    (dict(causal=-1), -2),
     (dict(scale=0.0), -7),
     (dict(scale=-1.0), -7),
     (dict(scale=float("nan")), -7),

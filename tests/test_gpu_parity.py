@@ -354,3 +354,54 @@ def test_mxfp8_rejects_bad_shapes(attn):
     s = torch.zeros(1, 1, 1, 4, dtype=torch.uint8, device="cuda")
     with pytest.raises(attn.AttnError, match="ATTN_E_SHAPE"):
         attn.fwd(q, q, q, q_scale=s, k_scale=s, v_scale=s)
+
+
+# ---------------------------------------------------------------------------
+# Causal alignment bottom-right (causal=2): key j is hidden from query i when
+# j > i + Nk - Nq; rows that see no key (Nq > Nk) must come out as O = 0 and
+# LSE = -inf, including whole workgroups with no key tile at all
+# ---------------------------------------------------------------------------
+def _compare_with_empty_rows(o, lse, o_ref, lse_ref, dtype, what, tol_rows=None):
+    oh, lh = host64(o), host64(lse)
+    empty = ~np.isfinite(lse_ref)
+    assert np.array_equal(~np.isfinite(lh), empty), what
+    assert np.all(oh[empty] == 0.0), what
+    full = ~empty
+    d_o = np.abs(oh - o_ref).max(axis=-1)
+    tol = TOL_O[dtype] if tol_rows is None else np.maximum(TOL_O[dtype], tol_rows)
+    err_o = d_o[full].max() if full.any() else 0.0
+    err_l = np.abs(lh[full] - lse_ref[full]).max() if full.any() else 0.0
+    announce(f"{what}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} empty rows={int(empty.sum())}")
+    assert np.all(np.isfinite(d_o[full])) and np.all((d_o <= tol)[full]) and err_l <= TOL_LSE, what
+
+
+@pytest.mark.parametrize("name", ["bf16_b4h16_n4096_d128", "bf16_b2h32_n8192_d64_causal_spiky",
+                                  "fp32_b1h1_n128_d64"])
+@pytest.mark.parametrize("nq,nk", [(100, 333), (333, 100), (600, 100), (1, 300), (300, 1), (256, 256)])
+def test_bottom_right_parity(attn, name, nq, nk):
+    w = WORKLOADS[name]
+    what = f"{name} bottom-right Nq={nq} Nk={nk}"
+    announce(what)
+    x = make_inputs(w, B=1, H=2, Nq=nq, Nk=nk)
+    o_ref, lse_ref = attention_f64(x["q64"], x["k64"], x["v64"], causal="bottom_right")
+    o, lse = run_fwd(attn, to_device(x), "bottom_right", "hw", 8.0)
+    _compare_with_empty_rows(o, lse, o_ref, lse_ref, w.dtype, what)
+
+
+@pytest.mark.parametrize("nq,nk", [(96, 352), (352, 96), (512, 64)])
+def test_mxfp8_bottom_right_parity(attn, nq, nk):
+    what = f"mxfp8 bottom-right Nq={nq} Nk={nk}"
+    announce(what)
+    x = make_inputs(MX, B=1, H=2, Nq=nq, Nk=nk)
+    o_ref, lse_ref = attention_f64(x["q64"], x["k64"], x["v64"], causal="bottom_right")
+    o, lse = run_fwd(attn, to_device(x), "bottom_right", "hw", 0.0)
+    # short rows do not average out P's e4m3 rounding: 2^-4 * max |v| over the
+    # keys a row sees (the bound of the top-left MXFP8 test)
+    v = x["v64"]
+    tol_rows = np.zeros(lse_ref.shape)
+    for h in range(v.shape[1]):
+        for i in range(nq):
+            n = min(nk, i + nk - nq + 1)
+            if n > 0:
+                tol_rows[0, h, i] = E4M3_REL * np.abs(v[0, h, :n]).max()
+    _compare_with_empty_rows(o, lse, o_ref, lse_ref, "mxfp8", what, tol_rows)
