@@ -24,7 +24,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "make_inputs", "bf16_bits", "bf16_bits_to_f32",
     "e4m3_decode_table", "e4m3_encode", "e8m0_for_amax", "mx_quantize",
-    "mx_dequantize", "make_score_inputs",
+    "mx_dequantize", "make_score_inputs", "make_packed_inputs",
 ]
 
 
@@ -233,3 +233,29 @@ def make_score_inputs(sigma: float, seed: int, rows: int = 256, keys: int = 8192
     scores = rng.standard_normal((rows, keys)) * sigma
     v = rng.standard_normal((keys, d))
     return scores, v
+
+
+def make_packed_inputs(w: Workload | str, q_lens, k_lens, H: int, seed: int):
+    """A packed batch of sequences of different lengths in the workload's dtype
+    (f32 or bf16): Q [total_q, H, d], K and V [total_k, H, d] token-major,
+    drawn as float32 standard normals in the order Q, K, V from
+    default_rng(seed); cu_q / cu_k int32 [B+1] sequence starts. Also returns
+    the exact float64 values (q64, k64, v64) the kernel receives."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((int(cu_q[-1]), H, w.d), dtype=np.float32)
+    k = rng.standard_normal((int(cu_k[-1]), H, w.d), dtype=np.float32)
+    v = rng.standard_normal((int(cu_k[-1]), H, w.d), dtype=np.float32)
+    out = {"cu_q": cu_q, "cu_k": cu_k, "H": H, "d": w.d, "dtype": w.dtype}
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if w.dtype == "f32":
+            out[n], out[n + "64"] = t, t.astype(np.float64)
+        elif w.dtype == "bf16":
+            bits = bf16_bits(t)
+            out[n], out[n + "64"] = bits, bf16_bits_to_f32(bits).astype(np.float64)
+        else:
+            raise ValueError("packed batches are defined for f32 and bf16")
+    return out

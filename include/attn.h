@@ -157,6 +157,34 @@ int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE
                 void* stream);
 
 /*
+ * attn_fwd_varlen -- a batch of sequences of different lengths, packed.
+ *
+ *   Q, O      device [total_q, H, d] (token-major: row t of head h at (t*H + h)*d)
+ *   K, V      device [total_k, H, d]
+ *   LSE       device float32 [H, total_q] (written)
+ *   cu_seqlens_q, cu_seqlens_k
+ *             device int32 arrays of B+1 entries: sequence b owns query rows
+ *             cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows
+ *             cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 (non-decreasing, starting at 0,
+ *             ending at total_q / total_k). Each sequence is one attention problem
+ *             with its own Nq and Nk; causal alignment (1 = top-left, 2 =
+ *             bottom-right) applies per sequence. A sequence with no keys gets
+ *             O = 0 and LSE = -inf. Offsets outside [0, total] are clamped, so
+ *             inconsistent arrays shorten sequences but never move an access
+ *             outside the tensors.
+ *   max_seqlen_q  >= every query length (query tiles past it are not computed)
+ *   dtype     ATTN_F32 or ATTN_BF16; other arguments as for attn_fwd.
+ * The kernels are those of attn_fwd_ex; only the addressing of each (sequence,
+ * head) slice differs. Source for the method: as attn_fwd. Validation that
+ * needs the lengths themselves cannot be done on the host (they live on the
+ * device); every other check happens before any launch.
+ */
+int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                    int max_seqlen_q, int total_q, int total_k, int d, int causal,
+                    float scale, int exp2_mode, float tau, int dtype, void* stream);
+
+/*
  * attn_fwd_stats -- attn_fwd_ex that also counts lagging-max rescale events.
  *
  *   stats     device uint64 [4], accumulated into (the caller zeroes it):

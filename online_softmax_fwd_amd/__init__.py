@@ -21,7 +21,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_stats", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
+__all__ = ["fwd", "fwd_varlen", "fwd_stats", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
            "ATTN_F32", "ATTN_BF16", "ATTN_MXFP8_E4M3", "ATTN_MXFP8_E4M3_PFIX_E4M3", "ATTN_MXFP8_E4M3_PFIX_E5M2",
            "EXP2_MODES", "STATUS"]
 
@@ -63,6 +63,8 @@ def load_library():
     lib.attn_fwd_ex.argtypes = fwd_args + [ci, vp, vp, vp, vp]
     lib.attn_fwd_ex.restype = ci
     lib.attn_fwd_stats.argtypes = fwd_args + [ci, vp, vp, vp, vp, vp]
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, cf, ci, vp]
+    lib.attn_fwd_varlen.restype = ci
     lib.attn_fwd_stats.restype = ci
     lib.attn_exp2.argtypes = [vp, vp, ctypes.c_long, ci, vp]
     lib.attn_exp2.restype = ci
@@ -159,6 +161,47 @@ def fwd(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 
     _check(lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                            B, H, Nq, k.shape[2], d, _causal(causal), scale, _mode(exp2_mode), float(tau),
                            dtype, scales[0], scales[1], scales[2], _stream_ptr(stream, q.device)))
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal=False, scale=None,
+               exp2_mode="hw", tau: float = 8.0, out=None, lse=None, stream=None):
+    """Packed batch of sequences of different lengths through attn_fwd_varlen.
+
+    q: [total_q, H, d], k, v: [total_k, H, d] (float32 or bfloat16, contiguous);
+    cu_seqlens_q / cu_seqlens_k: int32 GPU tensors [B+1] of sequence starts.
+    Returns O [total_q, H, d] and LSE [H, total_q]."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D GPU tensor [total, H, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share a dtype")
+    dtype = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}.get(q.dtype)
+    if dtype is None:
+        raise ValueError(f"unsupported dtype {q.dtype} for packed batches")
+    total_q, H, d = q.shape
+    total_k = k.shape[0]
+    if k.shape[1:] != (H, d) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for name, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not c.is_cuda or c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor [B+1]")
+    B = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_k.shape[0] != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse has the wrong shape, dtype or layout")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, int(max_seqlen_q),
+                               total_q, total_k, d, _causal(causal), scale, _mode(exp2_mode), float(tau), dtype,
+                               _stream_ptr(stream, q.device)))
     return out, lse
 
 

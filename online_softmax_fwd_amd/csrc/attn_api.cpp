@@ -59,14 +59,10 @@ int mix_table(int dtype, int d, int causal) {
   }
 }
 
-int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                      int B, int H, int Nq, int Nk, int d, int causal, float scale, int exp2_mode, float tau,
-                      int dtype, const uint8_t* qs, const uint8_t* ks, const uint8_t* vs, bool* nothing) {
-  *nothing = false;
+// Checks shared by the dense and the packed entry points; sets *emu16.
+int validate_common(int dtype, int d, int causal, float scale, int exp2_mode, float tau, int* emu16) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16 && !is_mx(dtype))
     return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32, ATTN_BF16 or one of the ATTN_MXFP8 codes", dtype);
-  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
-    return fail(ATTN_E_SHAPE, "negative size (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
   if (d != 64 && d != 128) return fail(ATTN_E_HEADDIM, "head dim d=%d is not 64 or 128", d);
   if (causal < 0 || causal > 2)
     return fail(ATTN_E_SHAPE, "causal=%d is not 0 (none), 1 (top-left) or 2 (bottom-right)", causal);
@@ -83,21 +79,58 @@ int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void
       return fail(ATTN_E_TAU, "tau=%g: with P scaled by 2^%d, max_offset + tau must stay below log2(%g) = %.3f",
                   (double)tau, kPMaxOffset, pmax, std::log2(pmax));
   }
-  int emu16;
   if (exp2_mode == ATTN_EXP2_HW) {
-    emu16 = 0;
+    *emu16 = 0;
   } else if (exp2_mode == ATTN_EXP2_EMU) {
-    emu16 = 16;
+    *emu16 = 16;
   } else if (exp2_mode == ATTN_EXP2_MIX) {
-    emu16 = mix_table(dtype, d, causal != 0);
+    *emu16 = mix_table(dtype, d, causal != 0);
   } else if (exp2_mode >= ATTN_EXP2_MIX_BASE && exp2_mode <= ATTN_EXP2_MIX_BASE + 16) {
-    emu16 = exp2_mode - ATTN_EXP2_MIX_BASE;
+    *emu16 = exp2_mode - ATTN_EXP2_MIX_BASE;
   } else {
     return fail(ATTN_E_EXP2MODE, "exp2_mode=%d is not HW (0), EMU (1), MIX (2) or MIX_BASE+k (16..32)",
                 exp2_mode);
   }
-  if (emu16 < 0 || !attn::emu16_supported(emu16))
-    return fail(ATTN_E_EXP2MODE, "no kernel instance emulates %d/16 of the exponentials", emu16);
+  if (*emu16 < 0 || !attn::emu16_supported(*emu16))
+    return fail(ATTN_E_EXP2MODE, "no kernel instance emulates %d/16 of the exponentials", *emu16);
+  return ATTN_OK;
+}
+
+void fill(attn::FwdArgs& a, const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int Nq,
+          int Nk, int d, int causal, float scale, float tau, int emu16) {
+  a.q = Q;
+  a.k = K;
+  a.v = V;
+  a.o = O;
+  a.lse = LSE;
+  a.q_scale = a.k_scale = a.v_scale = nullptr;
+  a.stats = nullptr;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.causal = causal != 0;
+  a.bottom_right = causal == 2;
+  a.cu_q = a.cu_k = nullptr;
+  a.total_q = a.total_k = 0;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
+  a.tau = tau;
+  a.emu16 = emu16;
+}
+
+int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                      int B, int H, int Nq, int Nk, int d, int causal, float scale, int exp2_mode, float tau,
+                      int dtype, const uint8_t* qs, const uint8_t* ks, const uint8_t* vs, bool* nothing) {
+  *nothing = false;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && !is_mx(dtype))
+    return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32, ATTN_BF16 or one of the ATTN_MXFP8 codes", dtype);
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(ATTN_E_SHAPE, "negative size (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
+  int emu16;
+  const bool mx = is_mx(dtype);
+  const int rc = validate_common(dtype, d, causal, scale, exp2_mode, tau, &emu16);
+  if (rc != ATTN_OK) return rc;
 
   const long long rows = (long long)B * H * Nq;
   if (rows == 0) {
@@ -111,7 +144,6 @@ int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void
   // The kernels address one (batch, head) slice of Q, K or V through a buffer
   // resource with 32-bit byte offsets, up to one key tile past the end.
   const long long esize = dtype == ATTN_F32 ? 4 : dtype == ATTN_BF16 ? 2 : 1;
-  const bool mx = is_mx(dtype);
   if (((long long)std::max(Nq, Nk) + 256) * d * esize > 0x7FFFFFFFLL)
     return fail(ATTN_E_SHAPE, "one (batch, head) slice of Q, K or V must stay under 2 GiB (Nq=%d Nk=%d d=%d)", Nq,
                 Nk, d);
@@ -127,25 +159,10 @@ int validate_and_fill(attn::FwdArgs& a, const void* Q, const void* K, const void
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
     return fail(ATTN_E_ALIGN, "Q, K, V, O and LSE must be 16-byte aligned");
 
-  a.q = Q;
-  a.k = K;
-  a.v = V;
-  a.o = O;
-  a.lse = LSE;
+  fill(a, Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, tau, emu16);
   a.q_scale = qs;
   a.k_scale = ks;
   a.v_scale = vs;
-  a.stats = nullptr;
-  a.B = B;
-  a.H = H;
-  a.Nq = Nq;
-  a.Nk = Nk;
-  a.d = d;
-  a.causal = causal != 0;
-  a.diag = causal == 2 ? Nk - Nq : 0;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
-  a.tau = tau;
-  a.emu16 = emu16;
   return ATTN_OK;
 }
 
@@ -194,6 +211,44 @@ int attn_fwd_stats(const void* Q, const void* K, const void* V, void* O, float* 
   if ((reinterpret_cast<uintptr_t>(stats) & 7u) != 0) return fail(ATTN_E_ALIGN, "stats must be 8-byte aligned");
   if (nothing) return ATTN_OK;
   a.stats = stats;
+  return run(a, dtype, stream);
+}
+
+int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE, const int* cu_seqlens_q,
+                    const int* cu_seqlens_k, int B, int H, int max_seqlen_q, int total_q, int total_k, int d,
+                    int causal, float scale, int exp2_mode, float tau, int dtype, void* stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_E_DTYPE, "packed variable-length batches take ATTN_F32 or ATTN_BF16 (got dtype %d)", dtype);
+  if (B < 0 || H < 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0)
+    return fail(ATTN_E_SHAPE, "negative size (B=%d H=%d max_seqlen_q=%d total_q=%d total_k=%d)", B, H,
+                max_seqlen_q, total_q, total_k);
+  int emu16;
+  const int rc = validate_common(dtype, d, causal, scale, exp2_mode, tau, &emu16);
+  if (rc != ATTN_OK) return rc;
+  if ((long long)B * H * max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
+  if (max_seqlen_q > total_q)
+    return fail(ATTN_E_SHAPE, "max_seqlen_q=%d exceeds total_q=%d", max_seqlen_q, total_q);
+  const long long n_qt = (max_seqlen_q + 127) / 128;
+  if ((long long)B * H * n_qt > 0x7FFFFFFFLL)
+    return fail(ATTN_E_SHAPE, "sizes too large (B=%d H=%d max_seqlen_q=%d)", B, H, max_seqlen_q);
+  // every row of one head's sequence is addressed with 32-bit byte offsets
+  // from the sequence start, up to one key tile past the end
+  const long long esize = dtype == ATTN_F32 ? 4 : 2;
+  if (((long long)std::max(total_q, total_k) + 256) * H * d * esize > 0x7FFFFFFFLL)
+    return fail(ATTN_E_SHAPE, "packed Q, K or V must stay under 2 GiB (total_q=%d total_k=%d H=%d d=%d)",
+                total_q, total_k, H, d);
+  if (!Q || !K || !V || !O || !LSE || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(ATTN_E_NULLPTR, "Q, K, V, O, LSE, cu_seqlens_q and cu_seqlens_k must be non-NULL");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return fail(ATTN_E_ALIGN, "Q, K, V, O and LSE must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) | reinterpret_cast<uintptr_t>(cu_seqlens_k)) & 3u)
+    return fail(ATTN_E_ALIGN, "cu_seqlens_q and cu_seqlens_k must be 4-byte aligned");
+  attn::FwdArgs a;
+  fill(a, Q, K, V, O, LSE, B, H, max_seqlen_q, total_k, d, causal, scale, tau, emu16);
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
   return run(a, dtype, stream);
 }
 

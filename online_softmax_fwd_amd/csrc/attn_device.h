@@ -76,6 +76,41 @@ __device__ __forceinline__ int xcd_logical_id(int wg, int n) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
+// Where a (batch, head) slice lives. Dense tensors are [B, H, N, d]: slice bh
+// starts at bh * N * d with rows d apart. Packed variable-length batches
+// (cu_q != nullptr) are [total, H, d]: sequence b holds rows cu[b] .. cu[b+1]-1
+// of every head, so slice (b, h) starts at (cu[b] * H + h) * d with rows H * d
+// apart; its LSE entries start at h * total_q + cu_q[b] of an [H, total_q] array.
+// Sequence bounds are clamped to [0, total] so that inconsistent offsets can
+// only shorten a sequence, never move an access outside the tensors.
+struct Slice {
+  size_t qbase, kbase, lse;  // element offsets of row 0 (Q and O share a layout)
+  int Nq, Nk;                // rows of this slice
+  int rs;                    // elements between consecutive rows
+};
+__device__ __forceinline__ Slice slice_of(int bh, int H, int d, int Nq, int Nk, const int* cu_q, const int* cu_k,
+                                          int total_q, int total_k) {
+  Slice s;
+  if (cu_q == nullptr) {
+    s.qbase = (size_t)bh * Nq * d;
+    s.kbase = (size_t)bh * Nk * d;
+    s.lse = (size_t)bh * Nq;
+    s.Nq = Nq;
+    s.Nk = Nk;
+    s.rs = d;
+  } else {
+    const int b = bh / H, h = bh - b * H;
+    const int q0 = min(max(cu_q[b], 0), total_q), k0 = min(max(cu_k[b], 0), total_k);
+    s.Nq = min(max(cu_q[b + 1], q0), total_q) - q0;
+    s.Nk = min(max(cu_k[b + 1], k0), total_k) - k0;
+    s.qbase = ((size_t)q0 * H + h) * d;
+    s.kbase = ((size_t)k0 * H + h) * d;
+    s.lse = (size_t)h * total_q + q0;
+    s.rs = H * d;
+  }
+  return s;
+}
+
 // Causal query tiles differ in length: tile qt of a head needs its first
 // qt+1 tiles' worth of keys. When the heads split evenly over the 8 XCDs, XCD
 // x takes the heads bh = x (mod 8), all of whose tiles therefore share that

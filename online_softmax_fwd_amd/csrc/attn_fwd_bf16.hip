@@ -224,11 +224,12 @@ __device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&
 // V_j is issued at the start of half-phase 2j into the other buffer of each
 // pair and waited for at the end of half-phase 2j+1.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int EMU16>
+template <int D, bool CAUSAL, int EMU16, bool PACKED>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                      __bf16* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats,
-                     int H, int Nq, int Nk, int n_qt, float c, float tau, int diag) {
+                     int H, int Nq_dense, int Nk_dense, int n_qt, float c, float tau, int bottom_right,
+                     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
   using C = Cfg<D, 64, 8>;
   constexpr int BN = C::BN, KB = C::KB;
   __shared__ __attribute__((aligned(1024))) char kb0[C::TILE];
@@ -253,8 +254,16 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int q0 = qt * C::BM;
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + l32;
-  const size_t qbase = (size_t)bh * Nq * D;
-  const size_t kbase = (size_t)bh * Nk * D;
+  // PACKED: a sequence of a packed batch (rows H*D apart); else dense [B,H,N,D]
+  // with the row pitch a compile-time constant
+  const Slice sl = slice_of(bh, H, D, Nq_dense, Nk_dense, PACKED ? cu_q : nullptr, cu_k, total_q, total_k);
+  const int Nq = sl.Nq, Nk = sl.Nk;
+  if (PACKED && q0 >= Nq) return;  // a query tile past this sequence's end
+  const size_t qbase = sl.qbase, kbase = sl.kbase;
+  const int rs = PACKED ? sl.rs : D;  // elements between rows in memory
+  const int rsb = rs * 2;             // bytes between K/V rows
+  // causal: key j is hidden from query i when j > i + diag (top-left: diag = 0)
+  const int diag = bottom_right ? Nk - Nq : 0;
 
   // ---- per-lane constants --------------------------------------------------
   uint32_t koff[D / 16], voff[D / 32], kld[C::LOADS], vld[C::LOADS];
@@ -273,11 +282,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int i = 0; i < C::LOADS; ++i) {
       const int pos = 64 * (wave + 8 * i) + lane;
       const int r = pos / C::CH, p = pos % C::CH;
-      kld[i] = r * C::RB + 16 * (p ^ swz_k<D>(r));
-      vld[i] = r * C::RB + 16 * (p ^ swz_v<D>(r));
+      kld[i] = r * rsb + 16 * (p ^ swz_k<D>(r));
+      vld[i] = r * rsb + 16 * (p ^ swz_v<D>(r));
     }
   }
-  const int nrec = Nk * C::RB;
+  const int nrec = Nk * rsb;
+  const uint32_t tile_bytes = (uint32_t)BN * rsb;
   const u32x4 rk = raw_buffer_rsrc(K + kbase, (uint32_t)nrec);
   const u32x4 rv = raw_buffer_rsrc(V + kbase, (uint32_t)nrec);
 
@@ -285,7 +295,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   bf16x8 qf[D / 16];
   {
     const bool ok = qi < Nq;
-    const __bf16* qp = Q + qbase + (size_t)(ok ? qi : 0) * D + 8 * hh;
+    const __bf16* qp = Q + qbase + (size_t)(ok ? qi : 0) * rs + 8 * hh;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       const u32x4 w = ok ? *(const u32x4*)(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
@@ -299,12 +309,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int T = (kend + BN - 1) / BN;
   if (T <= 0) {  // no row of this workgroup sees a key (bottom-right, Nq > Nk)
     if (qi < Nq) {
-      __bf16* op = O + qbase + (size_t)qi * D + 4 * hh;
+      __bf16* op = O + qbase + (size_t)qi * rs + 4 * hh;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) *(bf16x4*)(op + 32 * db + 8 * g) = bf16x4{};
-      if (hh == 0) LSE[(size_t)bh * Nq + qi] = kNegInf;
+      if (hh == 0) LSE[sl.lse + qi] = kNegInf;
     }
     return;
   }
@@ -324,9 +334,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int i = 0; i < C::LOADS; ++i) {
       const int slot = 1024 * (wave + 8 * i);
       if (j + 1 < T)
-        dma16(rk, kdst + slot, kld[i] + (uint32_t)(j + 1) * C::TILE);
+        dma16(rk, kdst + slot, kld[i] + (uint32_t)(j + 1) * tile_bytes);
       if (j < T)
-        dma16(rv, vdst + slot, vld[i] + (uint32_t)j * C::TILE);
+        dma16(rv, vdst + slot, vld[i] + (uint32_t)j * tile_bytes);
     }
   };
 
@@ -432,7 +442,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const float l_tot = pl_sum_halves(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that saw no key: O = 0, LSE = -inf
   if (qi < Nq) {
-    __bf16* op = O + qbase + (size_t)qi * D + 4 * hh;
+    __bf16* op = O + qbase + (size_t)qi * rs + 4 * hh;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -442,7 +452,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[db][4 * g + r] * inv);
         *(bf16x4*)(op + 32 * db + 8 * g) = w;
       }
-    if (hh == 0) LSE[(size_t)bh * Nq + qi] = (m_run * c + __builtin_log2f(l_tot)) * 0.693147180559945309f;
+    if (hh == 0) LSE[sl.lse + qi] = (m_run * c + __builtin_log2f(l_tot)) * 0.693147180559945309f;
   }
   if (stats && lane == 0) {
 #pragma unroll
@@ -450,15 +460,20 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 }
 
+template <int D, bool CAUSAL, int EMU16, bool PACKED>
+hipError_t launch_k(const FwdArgs& a, hipStream_t stream) {
+  constexpr int BM = Cfg<D, 64, 8>::BM;
+  const int n_qt = (a.Nq + BM - 1) / BM;  // a.Nq: the longest sequence for packed batches
+  const long long grid = (long long)a.B * a.H * n_qt;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EMU16, PACKED>), dim3((unsigned)grid), dim3(512), 0, stream,
+                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.stats, a.H,
+                     a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.bottom_right, a.cu_q, a.cu_k, a.total_q, a.total_k);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, int EMU16>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  constexpr int BM = Cfg<D, 64, 8>::BM;
-  const int n_qt = (a.Nq + BM - 1) / BM;
-  const long long grid = (long long)a.B * a.H * n_qt;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EMU16>), dim3((unsigned)grid), dim3(512), 0, stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.stats, a.H,
-                     a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.diag);
-  return hipGetLastError();
+  return a.cu_q ? launch_k<D, CAUSAL, EMU16, true>(a, stream) : launch_k<D, CAUSAL, EMU16, false>(a, stream);
 }
 
 template <int D, bool CAUSAL>

@@ -36,11 +36,12 @@ __device__ __forceinline__ int key_of_row_f(int m) {
   return ((g >> 1) << 4) | (h << 3) | ((g & 1) << 2) | r;
 }
 
-template <int D, bool CAUSAL, int EMU16>
+template <int D, bool CAUSAL, int EMU16, bool PACKED>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
 void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                     float* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats,
-                    int H, int Nq, int Nk, int n_qt, float c, float tau, int diag) {
+                    int H, int Nq_dense, int Nk_dense, int n_qt, float c, float tau, int bottom_right,
+                    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
   using G = GeoF<D>;
   __shared__ __attribute__((aligned(16))) float smem[2 * G::bufElems];
 
@@ -57,13 +58,16 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kQW;
   const int qi = qw0 + l32;
-  const size_t qbase = (size_t)bh * Nq * D;
-  const size_t kbase = (size_t)bh * Nk * D;
+  const Slice sl = slice_of(bh, H, D, Nq_dense, Nk_dense, PACKED ? cu_q : nullptr, cu_k, total_q, total_k);
+  const int Nq = sl.Nq, Nk = sl.Nk;
+  if (PACKED && q0 >= Nq) return;  // a query tile past this sequence's end
+  const size_t qbase = sl.qbase, kbase = sl.kbase;
+  const int diag = bottom_right ? Nk - Nq : 0;
 
   float qf[D / 2];
   {
     const bool ok = qi < Nq;
-    const float* qp = Q + qbase + (size_t)(ok ? qi : 0) * D + (D / 2) * hh;
+    const float* qp = Q + qbase + (size_t)(ok ? qi : 0) * sl.rs + (D / 2) * hh;
 #pragma unroll
     for (int s = 0; s < D / 2; s += 4) {
       const floatx4 w = ok ? *(const floatx4*)(qp + s) : floatx4{0.f, 0.f, 0.f, 0.f};
@@ -84,7 +88,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
       const int ch = tid + i * kThreads;
       const int row = ch / (D / 4), col = ch % (D / 4);
       const bool ok = k0 + row < Nk;
-      const size_t off = kbase + (size_t)(k0 + row) * D + col * 4;
+      const size_t off = kbase + (size_t)(k0 + row) * sl.rs + col * 4;
       kreg[i] = ok ? *(const floatx4*)(K + off) : floatx4{0.f, 0.f, 0.f, 0.f};
       vreg[i] = ok ? *(const floatx4*)(V + off) : floatx4{0.f, 0.f, 0.f, 0.f};
     }
@@ -197,7 +201,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that saw no key: O = 0, LSE = -inf
   if (qi < Nq) {
-    float* op = O + qbase + (size_t)qi * D + 4 * hh;
+    float* op = O + qbase + (size_t)qi * sl.rs + 4 * hh;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -207,7 +211,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
         for (int r = 0; r < 4; ++r) w[r] = o[db][4 * g + r] * inv;
         *(floatx4*)(op + 32 * db + 8 * g) = w;
       }
-    if (hh == 0) LSE[(size_t)bh * Nq + qi] = (m_run * c + __builtin_log2f(l_tot)) * 0.693147180559945309f;
+    if (hh == 0) LSE[sl.lse + qi] = (m_run * c + __builtin_log2f(l_tot)) * 0.693147180559945309f;
   }
   if (stats && lane == 0) {
 #pragma unroll
@@ -215,14 +219,19 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
   }
 }
 
-template <int D, bool CAUSAL, int EMU16>
-hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+template <int D, bool CAUSAL, int EMU16, bool PACKED>
+hipError_t launch_k(const FwdArgs& a, hipStream_t stream) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
   const long long grid = (long long)a.B * a.H * n_qt;
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, EMU16>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, EMU16, PACKED>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.stats,
-                     a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.diag);
+                     a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.bottom_right, a.cu_q, a.cu_k, a.total_q, a.total_k);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, int EMU16>
+hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+  return a.cu_q ? launch_k<D, CAUSAL, EMU16, true>(a, stream) : launch_k<D, CAUSAL, EMU16, false>(a, stream);
 }
 
 template <int D, bool CAUSAL>

@@ -128,7 +128,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
                       const uint8_t* __restrict__ QS, const uint8_t* __restrict__ KS, const uint8_t* __restrict__ VS,
                       __bf16* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats, int H,
-                      int Nq, int Nk, int n_qt, float c, float tau, int diag) {
+                      int Nq, int Nk, int n_qt, float c, float tau, int bottom_right) {
   __shared__ __attribute__((aligned(1024))) char kb0[kTile];
   __shared__ __attribute__((aligned(1024))) char kb1[kTile];
   __shared__ __attribute__((aligned(1024))) char vb0[kTile];
@@ -200,7 +200,8 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   // byte 2s of (qsc >> 8h) is the scale of d block 2s + h: op_sel picks byte 2s
   const int qscale = (int)(qsc >> (8 * hh));
 
-  // causal: key j is hidden from query i when j > i + diag
+  // causal: key j is hidden from query i when j > i + diag (top-left: diag = 0)
+  const int diag = bottom_right ? Nk - Nq : 0;
   const int kend = CAUSAL ? min(Nk, q0 + kBM + diag) : Nk;
   const int n_kt = (kend + kBN - 1) / kBN;
 
@@ -383,7 +384,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const long long grid = (long long)a.B * a.H * n_qt;
   hipLaunchKernelGGL((fwd_mxfp8_kernel<CAUSAL, EMU16, PMODE>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_scale, a.k_scale, a.v_scale,
-                     (__bf16*)a.o, a.lse, a.stats, a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.diag);
+                     (__bf16*)a.o, a.lse, a.stats, a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.bottom_right);
   return hipGetLastError();
 }
 

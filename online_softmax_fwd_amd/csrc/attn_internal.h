@@ -19,7 +19,10 @@ struct FwdArgs {
   unsigned long long* stats;  // optional rescale counters (4 x uint64)
   int B, H, Nq, Nk, d;
   int causal;               // 0 or 1
-  int diag;                 // causal: key j hidden from query i when j > i + diag
+  int bottom_right;         // causal: key j hidden from query i when j > i + (Nk - Nq) instead of j > i
+  const int* cu_q;          // packed variable-length batch: sequence starts (B+1 entries), else nullptr
+  const int* cu_k;
+  int total_q, total_k;     // rows of the packed Q and K/V
   float scale_log2;         // scale * log2(e)
   float tau;                // lagging-max threshold, log2 units
   int emu16;                // software-exp2 share of P, in 16ths (0 = all hardware)

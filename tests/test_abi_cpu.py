@@ -28,8 +28,8 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert names == sorted(["attn_exp2", "attn_fwd", "attn_fwd_ex", "attn_fwd_stats", "attn_last_error",
-                            "attn_mix_sixteenths"])
+    assert names == sorted(["attn_exp2", "attn_fwd", "attn_fwd_ex", "attn_fwd_stats", "attn_fwd_varlen",
+                            "attn_last_error", "attn_mix_sixteenths"])
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {lib._name}").read()
@@ -129,3 +129,39 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         attn.fwd(x, x, x)
+
+
+def _varlen(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, cq=FAKE, ck=FAKE, B=2, H=4, maxq=100, tq=150, tk=170,
+             d=128, causal=0, scale=0.088, mode=0, tau=8.0, dtype=1)
+    a.update(kw)
+    return lib.attn_fwd_varlen(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["cq"], a["ck"], a["B"], a["H"],
+                               a["maxq"], a["tq"], a["tk"], a["d"], a["causal"], a["scale"], a["mode"], a["tau"],
+                               a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -4),              # packed batches take f32 or bf16
+    (dict(dtype=3), -4),
+    (dict(B=-1), -2),
+    (dict(tq=-5), -2),
+    (dict(maxq=200), -2),             # longer than the whole packed Q
+    (dict(d=96), -3),
+    (dict(causal=3), -2),
+    (dict(scale=0.0), -7),
+    (dict(tau=-1.0), -6),
+    (dict(mode=99), -5),
+    (dict(cq=None), -1),
+    (dict(ck=None), -1),
+    (dict(cq=FAKE + 2), -8),
+    (dict(O=FAKE + 4), -8),
+    (dict(tq=1 << 22, maxq=1 << 20), -2),   # packed Q of 2 GiB or more
+])
+def test_varlen_validation_errors(lib, kw, code):
+    assert _varlen(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(maxq=0), dict(tq=0, maxq=0)])
+def test_varlen_nothing_to_do(lib, kw):
+    assert _varlen(lib, Q=None, K=None, V=None, O=None, LSE=None, cq=None, ck=None, **kw) == 0

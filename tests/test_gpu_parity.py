@@ -405,3 +405,49 @@ def test_mxfp8_bottom_right_parity(attn, nq, nk):
             if n > 0:
                 tol_rows[0, h, i] = E4M3_REL * np.abs(v[0, h, :n]).max()
     _compare_with_empty_rows(o, lse, o_ref, lse_ref, "mxfp8", what, tol_rows)
+
+
+# ---------------------------------------------------------------------------
+# Packed batches of sequences of different lengths (attn_fwd_varlen): each
+# sequence against the oracle on its own rows; includes a sequence without
+# queries, one without keys (O = 0, LSE = -inf), one of a single row, and
+# lengths that are not multiples of the tiles
+# ---------------------------------------------------------------------------
+VARLEN_Q = [300, 1, 129, 0, 77, 256, 5]
+VARLEN_K = [333, 50, 129, 10, 0, 512, 700]
+
+
+@pytest.mark.parametrize("name", ["bf16_b4h16_n4096_d128", "bf16_b2h32_n8192_d64_causal_spiky",
+                                  "fp32_b1h1_n128_d64"])
+@pytest.mark.parametrize("causal", [False, "top_left", "bottom_right"])
+def test_varlen_parity(attn, name, causal):
+    import torch
+    from attn_inputs import make_packed_inputs
+    w = WORKLOADS[name]
+    what = f"{name} packed causal={causal}"
+    announce(what)
+    H = 3
+    x = make_packed_inputs(w, VARLEN_Q, VARLEN_K, H, seed=4242)
+    dev = torch.device("cuda", 0)
+    if w.dtype == "bf16":
+        q, k, v = (torch.from_numpy(x[n].view(np.int16)).to(dev).view(torch.bfloat16) for n in ("q", "k", "v"))
+    else:
+        q, k, v = (torch.from_numpy(x[n]).to(dev) for n in ("q", "k", "v"))
+    cq = torch.from_numpy(x["cu_q"]).to(dev)
+    ck = torch.from_numpy(x["cu_k"]).to(dev)
+    o, lse = attn.fwd_varlen(q, k, v, cq, ck, max(VARLEN_Q), causal=causal, exp2_mode="hw", tau=8.0)
+    oh, lh = host64(o), host64(lse)
+    for b, (nq, nk) in enumerate(zip(VARLEN_Q, VARLEN_K)):
+        if nq == 0:
+            continue
+        q0, k0 = x["cu_q"][b], x["cu_k"][b]
+        qs = x["q64"][q0:q0 + nq].transpose(1, 0, 2)[None]
+        ks = x["k64"][k0:k0 + nk].transpose(1, 0, 2)[None]
+        vs = x["v64"][k0:k0 + nk].transpose(1, 0, 2)[None]
+        if nk == 0:
+            assert np.all(oh[q0:q0 + nq] == 0.0) and np.all(lh[:, q0:q0 + nq] == -np.inf), (what, b)
+            continue
+        o_ref, lse_ref = attention_f64(qs, ks, vs, causal=causal)
+        _compare_with_empty_rows(torch.from_numpy(oh[q0:q0 + nq].transpose(1, 0, 2)[None].copy()),
+                                 torch.from_numpy(lh[:, q0:q0 + nq][None].copy()), o_ref, lse_ref, w.dtype,
+                                 f"{what} sequence {b} (Nq={nq}, Nk={nk})")
