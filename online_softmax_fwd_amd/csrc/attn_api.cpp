@@ -40,20 +40,19 @@ constexpr int kPMaxOffset = 8;  // P scale exponent of the fixed-scale FP8 P dty
 // (SQ_INSTS_VALU per launch), so moving work there only pays if the ALU has
 // idle issue slots. The entries are the fastest shares measured on MI355X
 // with these kernels (HIP-event medians after a 2 s warm-up, shares 0, 1, 2
-// and 4 sixteenths): bf16 d=128 non-causal and causal at B=4 H=16 N=4096 and
-// bf16 d=64 causal at B=2 H=32 N=8192 are fastest all-hardware; MXFP8
-// non-causal at B=2 H=16 N=8192 ties at 0 and 1 sixteenth (1/16 kept), causal
-// is fastest at 0. The float32 kernel follows the bf16 entries.
+// and 4 sixteenths): bf16 d=128 non-causal and causal at B=4 H=16 N=4096,
+// bf16 d=64 causal at B=2 H=32 N=8192 and MXFP8 at B=2 H=16 N=8192 (every P
+// mode) are all fastest all-hardware. The float32 kernel follows the bf16
+// entries.
 int mix_table(int dtype, int d, int causal) {
   if (d != 64 && d != 128) return -1;
   switch (dtype) {
     case ATTN_BF16:
     case ATTN_F32:
-      return 0;
     case ATTN_MXFP8_E4M3:
     case ATTN_MXFP8_E4M3_PFIX_E4M3:
     case ATTN_MXFP8_E4M3_PFIX_E5M2:
-      return causal ? 0 : 1;
+      return 0;
     default:
       return -1;
   }

@@ -104,7 +104,7 @@ __device__ __forceinline__ float sum16(const floatx16& x) {
 // E8M0 byte of the smallest power of two X with amax / X <= 448 (e4m3's
 // largest finite value), read off the float32 bits of amax >= 0: with
 // amax = 1.f * 2^e, X = 2^(e-8) when 1.f <= 1.75, else 2^(e-7). Zero gives
-// X = 1. Clamped to [1, 253] so 2^(127 - byte) is a normal float.
+// X = 1. Clamped to [1, 253] so X and 1/X are normal floats.
 __device__ __forceinline__ uint32_t e8m0_of(float amax) {
   const uint32_t u = __builtin_bit_cast(uint32_t, amax);
   const int eb = (int)((u >> 23) & 0xFF);
@@ -112,7 +112,6 @@ __device__ __forceinline__ uint32_t e8m0_of(float amax) {
   byte = eb == 0 ? 127 : byte;
   return (uint32_t)__builtin_amdgcn_fmed3f((float)byte, 1.0f, 253.0f);
 }
-__device__ __forceinline__ float inv_scale(uint32_t byte) { return __builtin_bit_cast(float, (254u - byte) << 23); }
 
 // P quantisation: kPBlock = one E8M0 scale per 32-key block from the block
 // amax (the MXFP8 page's design); kPFixedE4M3 / kPFixedE5M2 = P times the
@@ -124,7 +123,7 @@ enum { kPBlock = 0, kPFixedE4M3 = 1, kPFixedE5M2 = 2 };
 constexpr int kMaxOffset = 8;
 
 template <bool CAUSAL, int EMU16, int PMODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
 void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
                       const uint8_t* __restrict__ QS, const uint8_t* __restrict__ KS, const uint8_t* __restrict__ VS,
                       __bf16* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats, int H,
@@ -286,13 +285,11 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
     const float mc = (m_run > kNegInf) ? m_run * c : 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = exp2_sel<EMU16>(__builtin_fmaf(s[kb][e], c, -mc), e);
-    l_run = __builtin_fmaf(l_run, alpha, sum16(s[0]) + sum16(s[1]));
 
-    // P -> e4m3 per 32-key block; the block amax from the reused block max
+    // P -> e4m3 per 32-key block: the block amax from the reused block max
+    // (P is monotone in s), its E8M0 byte sb, and P / X with X = 2^(sb - 127)
+    // taken straight from the exponential, 2^(s*c - mc + 127 - sb), so the
+    // quantiser needs no multiply; l adds the block sums times X.
     uint32_t sb0, sb1;
     if constexpr (PMODE == kPBlock) {
       sb0 = e8m0_of(exp2_hw(__builtin_fmaf(bm0, c, -mc)));
@@ -300,21 +297,27 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
     } else {
       sb0 = sb1 = 127 - kMaxOffset;  // P is stored times 2^max_offset
     }
-    const float inv0 = inv_scale(sb0), inv1 = inv_scale(sb1);
+    const float bias0 = mc - (float)(127 - (int)sb0), bias1 = mc - (float)(127 - (int)sb1);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[0][e] = exp2_sel<EMU16>(__builtin_fmaf(s[0][e], c, -bias0), e);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[1][e] = exp2_sel<EMU16>(__builtin_fmaf(s[1][e], c, -bias1), e);
+    const float x0 = __builtin_bit_cast(float, sb0 << 23), x1 = __builtin_bit_cast(float, sb1 << 23);
+    l_run = __builtin_fmaf(l_run, alpha, __builtin_fmaf(sum16(s[0]), x0, sum16(s[1]) * x1));
     i32x8 pq;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       int lo = 0, hi = 0;
       if constexpr (PMODE == kPFixedE5M2) {
-        lo = __builtin_amdgcn_cvt_pk_bf8_f32(s[0][4 * w] * inv0, s[0][4 * w + 1] * inv0, lo, false);
-        lo = __builtin_amdgcn_cvt_pk_bf8_f32(s[0][4 * w + 2] * inv0, s[0][4 * w + 3] * inv0, lo, true);
-        hi = __builtin_amdgcn_cvt_pk_bf8_f32(s[1][4 * w] * inv1, s[1][4 * w + 1] * inv1, hi, false);
-        hi = __builtin_amdgcn_cvt_pk_bf8_f32(s[1][4 * w + 2] * inv1, s[1][4 * w + 3] * inv1, hi, true);
+        lo = __builtin_amdgcn_cvt_pk_bf8_f32(s[0][4 * w], s[0][4 * w + 1], lo, false);
+        lo = __builtin_amdgcn_cvt_pk_bf8_f32(s[0][4 * w + 2], s[0][4 * w + 3], lo, true);
+        hi = __builtin_amdgcn_cvt_pk_bf8_f32(s[1][4 * w], s[1][4 * w + 1], hi, false);
+        hi = __builtin_amdgcn_cvt_pk_bf8_f32(s[1][4 * w + 2], s[1][4 * w + 3], hi, true);
       } else {
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * w] * inv0, s[0][4 * w + 1] * inv0, lo, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * w + 2] * inv0, s[0][4 * w + 3] * inv0, lo, true);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * w] * inv1, s[1][4 * w + 1] * inv1, hi, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * w + 2] * inv1, s[1][4 * w + 3] * inv1, hi, true);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * w], s[0][4 * w + 1], lo, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * w + 2], s[0][4 * w + 3], lo, true);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * w], s[1][4 * w + 1], hi, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * w + 2], s[1][4 * w + 3], hi, true);
       }
       pq[w] = lo;
       pq[4 + w] = hi;
