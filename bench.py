@@ -41,14 +41,14 @@ DEFAULT_WORKLOAD = "bf16_b4h16_n4096_d128"
 # HBM traffic of one non-causal launch of the default workload, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch, --calib-copy-mib 256). Calibrated on a plain 256 MiB device copy in
-# the same runs: FETCH_SIZE read 131088.1 KiB for 262144 KiB moved (x2.0),
+# the same runs: FETCH_SIZE read 131088.8 KiB for 262144 KiB moved (x2.0),
 # WRITE_SIZE read 262144 KiB (x1.0). Valid only for the kernel sources it was
 # taken on (first 16 hex digits of their SHA-256); any edit turns it off.
 TRAFFIC = {
     "workload": "bf16_b4h16_n4096_d128",
-    "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "4966bc4dffc341df",
-                "online_softmax_fwd_amd/csrc/attn_device.h": "050377147c931413"},
-    "fetch_kib_raw": 98445.5, "fetch_scale": 2.0,
+    "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "be484923ac20791d",
+                "online_softmax_fwd_amd/csrc/attn_device.h": "ac8149acc05ef8a2"},
+    "fetch_kib_raw": 98458.7, "fetch_scale": 2.0,
     "write_kib_raw": 66560.0, "write_scale": 1.0,
 }
 
