@@ -4,6 +4,7 @@ Tolerances are the ones fixed for this path: max abs error of O 1e-4 (f32
 inputs), 2e-2 (bf16), 6e-2 (MXFP8); LSE 1e-3. The oracle sees the exact
 values the kernel receives (bf16 widened, MXFP8 dequantised).
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -218,19 +219,26 @@ def test_device_exp2_matches_model(attn):
     assert rel_hw.max() < 1e-6
 
 
+# Keys per tile of the bf16 kernels (the d = 64 streaming kernel and the
+# d = 128 ping-pong kernel); a lagging-max decision is taken once per tile.
+BF16_KEY_TILE = {64: 64, 128: 64}
+
+
 @pytest.mark.parametrize("tau", [0.0, 8.0])
 @pytest.mark.parametrize("causal", [False, True])
-def test_rescale_counts_match_oracle(attn, tau, causal):
+@pytest.mark.parametrize("d", [64, 128])
+def test_rescale_counts_match_oracle(attn, tau, causal, d):
     """The kernel's lagging-max decisions, counted per row and per 32-row
-    group, against the oracle's blockwise recurrence at the kernel's 64-key
+    group, against the oracle's blockwise recurrence at the kernel's key
     tiles. Near-ties may round differently, so a small slack is allowed."""
-    w = WORKLOADS["bf16_b2h32_n8192_d64_causal_spiky"]
+    w = dataclasses.replace(WORKLOADS["bf16_b2h32_n8192_d64_causal_spiky"], d=d)
     x = make_inputs(w, B=1, H=2, Nq=1024, Nk=2048)
     dev = to_device(x)
     _, _, st = attn.fwd_stats(dev["q"], dev["k"], dev["v"], causal=causal, exp2_mode="hw", tau=tau)
-    _, _, ref = blockwise_f64(x["q64"], x["k64"], x["v64"], causal=causal, block=64, tau=tau, group=32)
+    _, _, ref = blockwise_f64(x["q64"], x["k64"], x["v64"], causal=causal, block=BF16_KEY_TILE[d], tau=tau,
+                              group=32)
     rows_ref, groups_ref = int(ref["rows"].sum()), int(ref["groups"].sum())
-    announce(f"tau={tau} causal={causal}: kernel rescales rows={st[1]} groups={st[3]} "
+    announce(f"d={d} tau={tau} causal={causal}: kernel rescales rows={st[1]} groups={st[3]} "
              f"(steps {st[0]}/{st[2]}); oracle rows={rows_ref} groups={groups_ref}")
     assert abs(st[1] - rows_ref) <= max(2, 0.01 * rows_ref)
     assert abs(st[3] - groups_ref) <= max(2, 0.01 * groups_ref)
