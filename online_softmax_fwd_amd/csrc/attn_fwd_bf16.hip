@@ -462,21 +462,24 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
 
 // ---------------------------------------------------------------------------
-// Streaming kernel for d = 64. A workgroup of 8 waves owns 256 query rows
-// (32 per wave) and streams K and V in 64-key tiles through two LDS buffers;
-// each wave runs the S^T MFMAs, the softmax and the PV MFMAs of a tile in
-// order, with no cross-wave phases. At d = 64 a wave fits in ~120 VGPRs, so
-// two workgroups share a CU (four waves per SIMD) and each SIMD interleaves
-// four independent streams. At this head dim the softmax weighs twice as
-// much per MFMA as at d = 128, and this occupancy hides it better than the
-// ping-pong schedule of fwd_bf16_kernel (measured +17 % non-causal, +23 %
-// causal at B=2, H=32, N=8192); at d = 128 the two schedules measure equal
-// and the ping-pong kernel is kept. The per-tile steps and their sources are
-// those of fwd_bf16_kernel.
+// Streaming kernel: d = 64, and causal d = 128. Each wave owns 32 query rows
+// and runs the S^T MFMAs, the softmax and the PV MFMAs of a key tile in
+// order, with no cross-wave phases; K and V tiles stream through two LDS
+// buffers shared by the workgroup. Several workgroups share a CU, so each
+// SIMD interleaves three or four independent streams. Measured against the
+// ping-pong schedule of fwd_bf16_kernel: at d = 64, where the softmax weighs
+// twice as much per MFMA, +17 % non-causal and +23 % causal (B=2, H=32,
+// N=8192); at d = 128 +6 % causal and equal non-causal (B=4, H=16, N=4096),
+// so non-causal d = 128 keeps the ping-pong kernel. The per-tile steps and
+// their sources are those of fwd_bf16_kernel.
 // ---------------------------------------------------------------------------
+// d = 64: 8 waves x 64-key tiles, two workgroups per CU (~120 VGPRs).
+// d = 128: 4 waves x 32-key tiles, three workgroups per CU (~157 VGPRs, 32 KB
+// of LDS each); used for causal launches, where the 128-row workgroups also
+// balance the triangle's uneven work better than 256-row ones.
 template <int D>
-struct StreamCfg : Cfg<D, 64, 8> {
-  static constexpr int WAVES_PER_SIMD = D == 64 ? 4 : 2;
+struct StreamCfg : Cfg<D, D == 64 ? 64 : 32, D == 64 ? 8 : 4> {
+  static constexpr int WAVES_PER_SIMD = D == 64 ? 4 : 3;
 };
 
 template <int D, bool CAUSAL, int EMU16, bool PACKED>
@@ -706,7 +709,7 @@ hipError_t launch_k(const FwdArgs& a, hipStream_t stream) {
 
 template <int D, bool CAUSAL, int EMU16>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  if constexpr (D == 64)
+  if constexpr (D == 64 || CAUSAL)
     return a.cu_q ? launch_stream<D, CAUSAL, EMU16, true>(a, stream) : launch_stream<D, CAUSAL, EMU16, false>(a, stream);
   else
     return a.cu_q ? launch_k<D, CAUSAL, EMU16, true>(a, stream) : launch_k<D, CAUSAL, EMU16, false>(a, stream);

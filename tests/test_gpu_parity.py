@@ -219,9 +219,12 @@ def test_device_exp2_matches_model(attn):
     assert rel_hw.max() < 1e-6
 
 
-# Keys per tile of the bf16 kernels (the d = 64 streaming kernel and the
-# d = 128 ping-pong kernel); a lagging-max decision is taken once per tile.
-BF16_KEY_TILE = {64: 64, 128: 64}
+def bf16_key_tile(d, causal):
+    """Keys per tile of the bf16 kernel a launch runs (a lagging-max decision
+    is taken once per tile): the streaming kernel takes 64-key tiles at d = 64
+    and 32-key tiles for causal d = 128; the ping-pong kernel (non-causal
+    d = 128) takes 64-key tiles."""
+    return 32 if (d == 128 and causal) else 64
 
 
 @pytest.mark.parametrize("tau", [0.0, 8.0])
@@ -235,7 +238,7 @@ def test_rescale_counts_match_oracle(attn, tau, causal, d):
     x = make_inputs(w, B=1, H=2, Nq=1024, Nk=2048)
     dev = to_device(x)
     _, _, st = attn.fwd_stats(dev["q"], dev["k"], dev["v"], causal=causal, exp2_mode="hw", tau=tau)
-    _, _, ref = blockwise_f64(x["q64"], x["k64"], x["v64"], causal=causal, block=BF16_KEY_TILE[d], tau=tau,
+    _, _, ref = blockwise_f64(x["q64"], x["k64"], x["v64"], causal=causal, block=bf16_key_tile(d, causal), tau=tau,
                               group=32)
     rows_ref, groups_ref = int(ref["rows"].sum()), int(ref["groups"].sum())
     announce(f"d={d} tau={tau} causal={causal}: kernel rescales rows={st[1]} groups={st[3]} "
