@@ -22,7 +22,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "make_inputs", "bf16_bits", "bf16_bits_to_f32",
+    "Workload", "WORKLOADS", "make_inputs", "mx_quantize_packed", "mx_compact_offsets", "bf16_bits", "bf16_bits_to_f32",
     "e4m3_decode_table", "e4m3_encode", "e8m0_for_amax", "mx_quantize",
     "mx_dequantize", "make_score_inputs", "make_packed_inputs",
 ]
@@ -236,11 +236,13 @@ def make_score_inputs(sigma: float, seed: int, rows: int = 256, keys: int = 8192
 
 
 def make_packed_inputs(w: Workload | str, q_lens, k_lens, H: int, seed: int):
-    """A packed batch of sequences of different lengths in the workload's dtype
-    (f32 or bf16): Q [total_q, H, d], K and V [total_k, H, d] token-major,
-    drawn as float32 standard normals in the order Q, K, V from
-    default_rng(seed); cu_q / cu_k int32 [B+1] sequence starts. Also returns
-    the exact float64 values (q64, k64, v64) the kernel receives."""
+    """A packed batch of sequences of different lengths in the workload's dtype:
+    Q [total_q, H, d], K and V [total_k, H, d] token-major, drawn as float32
+    standard normals in the order Q, K, V from default_rng(seed); cu_q / cu_k
+    int32 [B+1] sequence starts. Also returns the exact float64 values
+    (q64, k64, v64) the kernel receives. MXFP8 adds the compact scales qs, ks,
+    vs [rows, H, d/32] (mx_quantize_packed) and their per-sequence first rows
+    sq_off / sk_off (mx_compact_offsets)."""
     if isinstance(w, str):
         w = WORKLOADS[w]
     cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
@@ -250,12 +252,50 @@ def make_packed_inputs(w: Workload | str, q_lens, k_lens, H: int, seed: int):
     k = rng.standard_normal((int(cu_k[-1]), H, w.d), dtype=np.float32)
     v = rng.standard_normal((int(cu_k[-1]), H, w.d), dtype=np.float32)
     out = {"cu_q": cu_q, "cu_k": cu_k, "H": H, "d": w.d, "dtype": w.dtype}
-    for n, t in (("q", q), ("k", k), ("v", v)):
+    for n, t, cu in (("q", q, cu_q), ("k", k, cu_k), ("v", v, cu_k)):
         if w.dtype == "f32":
             out[n], out[n + "64"] = t, t.astype(np.float64)
         elif w.dtype == "bf16":
             bits = bf16_bits(t)
             out[n], out[n + "64"] = bits, bf16_bits_to_f32(bits).astype(np.float64)
+        elif w.dtype == "mxfp8":
+            out[n], out[n + "s"], out[n + "64"] = mx_quantize_packed(t, cu)
         else:
-            raise ValueError("packed batches are defined for f32 and bf16")
+            raise ValueError(w.dtype)
+    if w.dtype == "mxfp8":
+        out["sq_off"] = mx_compact_offsets(cu_q)
+        out["sk_off"] = mx_compact_offsets(cu_k)
     return out
+
+
+def mx_compact_offsets(cu) -> np.ndarray:
+    """First row of each sequence in a compact packed scale tensor: the
+    exclusive prefix sum of ceil(len / 32), int32 [B+1]."""
+    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    return np.concatenate([[0], np.cumsum((lens + 31) // 32)]).astype(np.int32)
+
+
+def mx_quantize_packed(x: np.ndarray, cu):
+    """MX-quantise a packed [total, H, d] float32 tensor per sequence: 32x32
+    blocks of (tokens, d) start at each sequence's first token, a partial last
+    block is quantised as if padded with zeros (zeros change no amax). Returns
+    (e4m3 bytes [total, H, d], compact E8M0 scales [sum ceil(len/32), H, d/32],
+    exact float64 values [total, H, d])."""
+    total, H, d = x.shape
+    q = np.empty((total, H, d), dtype=np.uint8)
+    x64 = np.empty((total, H, d), dtype=np.float64)
+    scales = []
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        n = s1 - s0
+        if n == 0:
+            continue
+        npad = (n + 31) // 32 * 32
+        blk = np.zeros((H, npad, d), dtype=np.float32)
+        blk[:, :n] = x[s0:s1].transpose(1, 0, 2)
+        qb, sb = mx_quantize(blk)
+        q[s0:s1] = qb[:, :n].transpose(1, 0, 2)
+        x64[s0:s1] = mx_dequantize(qb, sb)[:, :n].transpose(1, 0, 2)
+        scales.append(sb.transpose(1, 0, 2))
+    sc = np.concatenate(scales) if scales else np.zeros((0, H, d // 32), dtype=np.uint8)
+    return q, np.ascontiguousarray(sc), x64

@@ -173,7 +173,8 @@ int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE
  *             inconsistent arrays shorten sequences but never move an access
  *             outside the tensors.
  *   max_seqlen_q  >= every query length (query tiles past it are not computed)
- *   dtype     ATTN_F32 or ATTN_BF16; other arguments as for attn_fwd.
+ *   dtype     ATTN_F32 or ATTN_BF16 (MXFP8 batches carry scales: attn_fwd_varlen_ex);
+ *             other arguments as for attn_fwd.
  * The kernels are those of attn_fwd_ex; only the addressing of each (sequence,
  * head) slice differs. Source for the method: as attn_fwd. Validation that
  * needs the lengths themselves cannot be done on the host (they live on the
@@ -183,6 +184,85 @@ int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float*
                     const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
                     int max_seqlen_q, int total_q, int total_k, int d, int causal,
                     float scale, int exp2_mode, float tau, int dtype, void* stream);
+
+/*
+ * attn_fwd_varlen_ex -- attn_fwd_varlen for every dtype, including packed MXFP8
+ * batches with split-addressed scale tensors.
+ *
+ * Source: "PyTorch FlashAttention-4 adds MXFP8 block-scaled forward and
+ * backward for Blackwell", section "Quantization along both axes and jagged
+ * tensors": with jagged sequences the FP8 data stays compact and only the
+ * scale tensors are laid out (padded) for the kernel.
+ *
+ *   Q, K, V, O, LSE, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_q, total_q,
+ *   total_k, d, causal, scale, exp2_mode, tau
+ *             as attn_fwd_varlen (Q, K, V are e4m3 bytes for MXFP8; O is bf16)
+ *   q_scale   device E8M0 bytes [scale_rows_q, H, d/32]: scale row
+ *             scale_offsets_q[b] + r, head h, byte c scales query rows
+ *             cu_seqlens_q[b] + 32r .. +31 (those inside the sequence) and
+ *             elements 32c .. 32c+31 of head h. Blocks start at each
+ *             sequence's first token, so a sequence's last block may be partial.
+ *   k_scale, v_scale
+ *             the same for K and V with scale_offsets_k and scale_rows_k
+ *   scale_offsets_q, scale_offsets_k
+ *             device int32 [B+1]: first scale row of each sequence (the rows
+ *             between ceil(len/32) and the next sequence's offset are padding
+ *             and are not read). attn_mx_scale_offsets writes them for the
+ *             compact (align 32) or a padded layout. Clamped to
+ *             [0, scale_rows]; blocks past scale_rows read as scale 1.
+ *   scale_rows_q, scale_rows_k   rows of the scale tensors (>= 0)
+ *   dtype     ATTN_F32, ATTN_BF16 or one of the MXFP8 codes; for F32/BF16 the
+ *             scale arguments are ignored and may be NULL / 0
+ * MXFP8 supports d = 128. Errors as attn_fwd_varlen; additionally
+ * ATTN_E_NULLPTR for a missing MXFP8 scale or offset pointer and ATTN_E_ALIGN
+ * for one that is not 4-byte aligned.
+ */
+int attn_fwd_varlen_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                       const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                       const int* cu_seqlens_q, const int* cu_seqlens_k,
+                       const int* scale_offsets_q, const int* scale_offsets_k,
+                       int scale_rows_q, int scale_rows_k, int B, int H, int max_seqlen_q,
+                       int total_q, int total_k, int d, int causal, float scale, int exp2_mode,
+                       float tau, int dtype, void* stream);
+
+/*
+ * attn_mx_scale_offsets -- first scale row of each packed sequence.
+ *
+ * Source: as attn_fwd_varlen_ex (the scale tensors of a jagged batch are
+ * padded to aligned positions while the data stays compact).
+ *
+ *   cu_seqlens  device int32 [B+1] sequence starts (clamped to [0, total])
+ *   align       rows of sequence alignment, a multiple of 32 in [32, 4096]:
+ *               32 gives the compact layout, 128 the page's padded one
+ *   offsets     device int32 [B+1] (written): offsets[b] = sum over b' < b of
+ *               ceil(len(b') / align) * align / 32; offsets[B] is the number
+ *               of scale rows the layout needs
+ * One small kernel on `stream`; ATTN_E_SHAPE when the row count could
+ * overflow int32, ATTN_E_NULLPTR / ATTN_E_ALIGN for bad pointers.
+ */
+int attn_mx_scale_offsets(const int* cu_seqlens, int B, int total, int align, int* offsets,
+                          void* stream);
+
+/*
+ * attn_mx_scale_scatter -- copy packed MXFP8 scales from one layout into
+ * another (e.g. compact jagged into 128-aligned padded rows).
+ *
+ * Source: as attn_fwd_varlen_ex (the scatter/layout kernels that move scales
+ * from the compact jagged layout into the padded one).
+ *
+ *   src, dst    device E8M0 bytes [src_rows, H, d/32] / [dst_rows, H, d/32]
+ *   src_offsets, dst_offsets
+ *               device int32 [B+1] first scale row of each sequence
+ *   cu_seqlens  device int32 [B+1] sequence starts (clamped to [0, total])
+ * Destination rows dst_offsets[b] .. dst_offsets[b+1]-1 (clamped to
+ * [0, dst_rows]) receive sequence b's ceil(len/32) rows from src_offsets[b]
+ * in order; the rest of that range, and rows whose source lies outside
+ * [0, src_rows), are set to 127 (scale 1). dst must not overlap src.
+ * d = 128 only (ATTN_E_HEADDIM otherwise); pointers 4-byte aligned.
+ */
+int attn_mx_scale_scatter(const uint8_t* src, const int* src_offsets, int src_rows, uint8_t* dst,
+                          const int* dst_offsets, int dst_rows, const int* cu_seqlens, int B,
+                          int total, int H, int d, void* stream);
 
 /*
  * attn_fwd_stats -- attn_fwd_ex that also counts lagging-max rescale events.

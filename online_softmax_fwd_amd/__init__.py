@@ -21,7 +21,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_varlen", "fwd_stats", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
+__all__ = ["fwd", "fwd_varlen", "fwd_stats", "mx_scale_offsets", "mx_scale_scatter", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
            "ATTN_F32", "ATTN_BF16", "ATTN_MXFP8_E4M3", "ATTN_MXFP8_E4M3_PFIX_E4M3", "ATTN_MXFP8_E4M3_PFIX_E5M2",
            "EXP2_MODES", "STATUS"]
 
@@ -65,6 +65,12 @@ def load_library():
     lib.attn_fwd_stats.argtypes = fwd_args + [ci, vp, vp, vp, vp, vp]
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, cf, ci, vp]
     lib.attn_fwd_varlen.restype = ci
+    lib.attn_fwd_varlen_ex.argtypes = [vp] * 12 + [ci] * 9 + [cf, ci, cf, ci, vp]
+    lib.attn_fwd_varlen_ex.restype = ci
+    lib.attn_mx_scale_offsets.argtypes = [vp, ci, ci, ci, vp, vp]
+    lib.attn_mx_scale_offsets.restype = ci
+    lib.attn_mx_scale_scatter.argtypes = [vp, vp, ci, vp, vp, ci, vp, ci, ci, ci, ci, vp]
+    lib.attn_mx_scale_scatter.restype = ci
     lib.attn_fwd_stats.restype = ci
     lib.attn_exp2.argtypes = [vp, vp, ctypes.c_long, ci, vp]
     lib.attn_exp2.restype = ci
@@ -164,13 +170,26 @@ def fwd(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 
     return out, lse
 
 
-def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal=False, scale=None,
-               exp2_mode="hw", tau: float = 8.0, out=None, lse=None, stream=None):
-    """Packed batch of sequences of different lengths through attn_fwd_varlen.
+def _int32_vec(name, c, n=None):
+    import torch
+    if not c.is_cuda or c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor [B+1]")
+    if n is not None and c.shape[0] != n:
+        raise ValueError(f"{name} must have {n} entries")
 
-    q: [total_q, H, d], k, v: [total_k, H, d] (float32 or bfloat16, contiguous);
-    cu_seqlens_q / cu_seqlens_k: int32 GPU tensors [B+1] of sequence starts.
-    Returns O [total_q, H, d] and LSE [H, total_q]."""
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal=False, scale=None,
+               exp2_mode="hw", tau: float = 8.0, out=None, lse=None, stream=None, q_scale=None, k_scale=None,
+               v_scale=None, scale_offsets_q=None, scale_offsets_k=None, fp8_p="block"):
+    """Packed batch of sequences of different lengths through attn_fwd_varlen_ex.
+
+    q: [total_q, H, d], k, v: [total_k, H, d] (float32, bfloat16, or uint8 e4m3
+    bytes for MXFP8; contiguous); cu_seqlens_q / cu_seqlens_k: int32 GPU
+    tensors [B+1] of sequence starts. MXFP8 also takes q_scale [rows_q, H, d/32]
+    and k_scale / v_scale [rows_k, H, d/32] uint8 E8M0 with each sequence's
+    first scale row in scale_offsets_q / scale_offsets_k (int32 [B+1], e.g.
+    from mx_scale_offsets). Returns O [total_q, H, d] (bfloat16 for MXFP8) and
+    LSE [H, total_q]."""
     import torch
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -178,31 +197,88 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal=Fa
             raise ValueError(f"{name} must be a contiguous 3-D GPU tensor [total, H, d]")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must share a dtype")
-    dtype = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}.get(q.dtype)
-    if dtype is None:
+    if q.dtype == torch.float32:
+        dtype, odt = ATTN_F32, torch.float32
+    elif q.dtype == torch.bfloat16:
+        dtype, odt = ATTN_BF16, torch.bfloat16
+    elif q.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        if fp8_p not in FP8_P:
+            raise ValueError(f"fp8_p must be one of {sorted(FP8_P)}")
+        dtype, odt = FP8_P[fp8_p], torch.bfloat16
+    else:
         raise ValueError(f"unsupported dtype {q.dtype} for packed batches")
     total_q, H, d = q.shape
     total_k = k.shape[0]
     if k.shape[1:] != (H, d) or v.shape != k.shape:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    for name, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
-        if not c.is_cuda or c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous int32 GPU tensor [B+1]")
+    _int32_vec("cu_seqlens_q", cu_seqlens_q)
     B = cu_seqlens_q.shape[0] - 1
-    if cu_seqlens_k.shape[0] != B + 1:
-        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
-    out = torch.empty_like(q) if out is None else out
+    _int32_vec("cu_seqlens_k", cu_seqlens_k, B + 1)
+    out = torch.empty((total_q, H, d), dtype=odt, device=q.device) if out is None else out
     lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+    if out.shape != q.shape or out.dtype != odt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
     if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse has the wrong shape, dtype or layout")
+    ptrs, rows = [0] * 5, [0, 0]
+    if dtype in FP8_P.values():
+        for i, (name, t) in enumerate((("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale))):
+            if t is None or t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 3 or \
+                    tuple(t.shape[1:]) != (H, d // 32):
+                raise ValueError(f"{name} must be contiguous uint8 [rows, H, d/32]")
+            ptrs[i] = t.data_ptr()
+        if v_scale.shape != k_scale.shape:
+            raise ValueError("k_scale and v_scale must have the same shape")
+        for i, (name, t) in enumerate((("scale_offsets_q", scale_offsets_q), ("scale_offsets_k", scale_offsets_k))):
+            if t is None:
+                raise ValueError(f"MXFP8 needs {name}")
+            _int32_vec(name, t, B + 1)
+            ptrs[3 + i] = t.data_ptr()
+        rows = [q_scale.shape[0], k_scale.shape[0]]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(lib.attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                               cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, int(max_seqlen_q),
-                               total_q, total_k, d, _causal(causal), scale, _mode(exp2_mode), float(tau), dtype,
-                               _stream_ptr(stream, q.device)))
+    _check(lib.attn_fwd_varlen_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                  ptrs[0], ptrs[1], ptrs[2], cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                                  ptrs[3], ptrs[4], rows[0], rows[1], B, H, int(max_seqlen_q), total_q, total_k, d,
+                                  _causal(causal), scale, _mode(exp2_mode), float(tau), dtype,
+                                  _stream_ptr(stream, q.device)))
     return out, lse
+
+
+def mx_scale_offsets(cu_seqlens, total: int, align: int = 32, out=None, stream=None):
+    """First scale row of each packed sequence (attn_mx_scale_offsets): int32
+    GPU tensor [B+1]; entry B is the number of scale rows. align 32 gives the
+    compact layout, 128 the padded one."""
+    import torch
+    lib = load_library()
+    _int32_vec("cu_seqlens", cu_seqlens)
+    B = cu_seqlens.shape[0] - 1
+    out = torch.empty(B + 1, dtype=torch.int32, device=cu_seqlens.device) if out is None else out
+    _int32_vec("out", out, B + 1)
+    _check(lib.attn_mx_scale_offsets(cu_seqlens.data_ptr(), B, int(total), int(align), out.data_ptr(),
+                                     _stream_ptr(stream, cu_seqlens.device)))
+    return out
+
+
+def mx_scale_scatter(src, src_offsets, dst_offsets, dst_rows: int, cu_seqlens, total: int, out=None, stream=None):
+    """Copy packed MX scales [src_rows, H, d/32] into the layout given by
+    dst_offsets (attn_mx_scale_scatter); padding rows get 127 (scale 1).
+    Returns the [dst_rows, H, d/32] uint8 GPU tensor."""
+    import torch
+    lib = load_library()
+    if not src.is_cuda or src.dtype != torch.uint8 or src.dim() != 3 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous uint8 GPU tensor [rows, H, d/32]")
+    _int32_vec("cu_seqlens", cu_seqlens)
+    B = cu_seqlens.shape[0] - 1
+    _int32_vec("src_offsets", src_offsets, B + 1)
+    _int32_vec("dst_offsets", dst_offsets, B + 1)
+    H, w = src.shape[1], src.shape[2]
+    out = torch.empty((int(dst_rows), H, w), dtype=torch.uint8, device=src.device) if out is None else out
+    if tuple(out.shape) != (int(dst_rows), H, w) or out.dtype != torch.uint8 or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    _check(lib.attn_mx_scale_scatter(src.data_ptr(), src_offsets.data_ptr(), src.shape[0], out.data_ptr(),
+                                     dst_offsets.data_ptr(), int(dst_rows), cu_seqlens.data_ptr(), B, int(total), H,
+                                     32 * w, _stream_ptr(stream, src.device)))
+    return out
 
 
 def fwd_stats(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 8.0,

@@ -28,6 +28,7 @@ SOURCES = [
     "attn_fwd_bf16.hip",
     "attn_fwd_f32.hip",
     "attn_fwd_mxfp8.hip",
+    "attn_mx_layout.hip",
 ]
 
 COMMON_FLAGS = [

@@ -113,6 +113,8 @@ void fill(attn::FwdArgs& a, const void* Q, const void* K, const void* V, void* O
   a.bottom_right = causal == 2;
   a.cu_q = a.cu_k = nullptr;
   a.total_q = a.total_k = 0;
+  a.scale_off_q = a.scale_off_k = nullptr;
+  a.scale_rows_q = a.scale_rows_k = 0;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
   a.tau = tau;
   a.emu16 = emu16;
@@ -213,17 +215,21 @@ int attn_fwd_stats(const void* Q, const void* K, const void* V, void* O, float* 
   return run(a, dtype, stream);
 }
 
-int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE, const int* cu_seqlens_q,
-                    const int* cu_seqlens_k, int B, int H, int max_seqlen_q, int total_q, int total_k, int d,
-                    int causal, float scale, int exp2_mode, float tau, int dtype, void* stream) {
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
-    return fail(ATTN_E_DTYPE, "packed variable-length batches take ATTN_F32 or ATTN_BF16 (got dtype %d)", dtype);
-  if (B < 0 || H < 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0)
-    return fail(ATTN_E_SHAPE, "negative size (B=%d H=%d max_seqlen_q=%d total_q=%d total_k=%d)", B, H,
-                max_seqlen_q, total_q, total_k);
+int attn_fwd_varlen_ex(const void* Q, const void* K, const void* V, void* O, float* LSE, const uint8_t* q_scale,
+                       const uint8_t* k_scale, const uint8_t* v_scale, const int* cu_seqlens_q,
+                       const int* cu_seqlens_k, const int* scale_offsets_q, const int* scale_offsets_k,
+                       int scale_rows_q, int scale_rows_k, int B, int H, int max_seqlen_q, int total_q, int total_k,
+                       int d, int causal, float scale, int exp2_mode, float tau, int dtype, void* stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && !is_mx(dtype))
+    return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32, ATTN_BF16 or one of the ATTN_MXFP8 codes", dtype);
+  const bool mx = is_mx(dtype);
+  if (B < 0 || H < 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0 || (mx && (scale_rows_q < 0 || scale_rows_k < 0)))
+    return fail(ATTN_E_SHAPE, "negative size (B=%d H=%d max_seqlen_q=%d total_q=%d total_k=%d scale rows %d/%d)", B,
+                H, max_seqlen_q, total_q, total_k, scale_rows_q, scale_rows_k);
   int emu16;
   const int rc = validate_common(dtype, d, causal, scale, exp2_mode, tau, &emu16);
   if (rc != ATTN_OK) return rc;
+  if (mx && d != 128) return fail(ATTN_E_HEADDIM, "MXFP8 supports d=128 (got %d)", d);
   if ((long long)B * H * max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
   if (max_seqlen_q > total_q)
     return fail(ATTN_E_SHAPE, "max_seqlen_q=%d exceeds total_q=%d", max_seqlen_q, total_q);
@@ -232,23 +238,86 @@ int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float*
     return fail(ATTN_E_SHAPE, "sizes too large (B=%d H=%d max_seqlen_q=%d)", B, H, max_seqlen_q);
   // every row of one head's sequence is addressed with 32-bit byte offsets
   // from the sequence start, up to one key tile past the end
-  const long long esize = dtype == ATTN_F32 ? 4 : 2;
+  const long long esize = dtype == ATTN_F32 ? 4 : dtype == ATTN_BF16 ? 2 : 1;
   if (((long long)std::max(total_q, total_k) + 256) * H * d * esize > 0x7FFFFFFFLL)
     return fail(ATTN_E_SHAPE, "packed Q, K or V must stay under 2 GiB (total_q=%d total_k=%d H=%d d=%d)",
                 total_q, total_k, H, d);
   if (!Q || !K || !V || !O || !LSE || !cu_seqlens_q || !cu_seqlens_k)
     return fail(ATTN_E_NULLPTR, "Q, K, V, O, LSE, cu_seqlens_q and cu_seqlens_k must be non-NULL");
+  if (mx && (!q_scale || !k_scale || !v_scale || !scale_offsets_q || !scale_offsets_k))
+    return fail(ATTN_E_NULLPTR, "MXFP8 needs q_scale, k_scale, v_scale, scale_offsets_q and scale_offsets_k");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
     return fail(ATTN_E_ALIGN, "Q, K, V, O and LSE must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) | reinterpret_cast<uintptr_t>(cu_seqlens_k)) & 3u)
-    return fail(ATTN_E_ALIGN, "cu_seqlens_q and cu_seqlens_k must be 4-byte aligned");
+  uintptr_t small = reinterpret_cast<uintptr_t>(cu_seqlens_q) | reinterpret_cast<uintptr_t>(cu_seqlens_k);
+  if (mx)
+    small |= reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+             reinterpret_cast<uintptr_t>(v_scale) | reinterpret_cast<uintptr_t>(scale_offsets_q) |
+             reinterpret_cast<uintptr_t>(scale_offsets_k);
+  if (small & 3u)
+    return fail(ATTN_E_ALIGN, "cu_seqlens, MX scale and scale offset pointers must be 4-byte aligned");
   attn::FwdArgs a;
   fill(a, Q, K, V, O, LSE, B, H, max_seqlen_q, total_k, d, causal, scale, tau, emu16);
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.total_q = total_q;
   a.total_k = total_k;
+  if (mx) {
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.scale_off_q = scale_offsets_q;
+    a.scale_off_k = scale_offsets_k;
+    a.scale_rows_q = scale_rows_q;
+    a.scale_rows_k = scale_rows_k;
+  }
   return run(a, dtype, stream);
+}
+
+int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE, const int* cu_seqlens_q,
+                    const int* cu_seqlens_k, int B, int H, int max_seqlen_q, int total_q, int total_k, int d,
+                    int causal, float scale, int exp2_mode, float tau, int dtype, void* stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_E_DTYPE, "attn_fwd_varlen takes ATTN_F32 or ATTN_BF16 (got dtype %d); MXFP8 batches need "
+                "their scales: attn_fwd_varlen_ex", dtype);
+  return attn_fwd_varlen_ex(Q, K, V, O, LSE, nullptr, nullptr, nullptr, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr,
+                            0, 0, B, H, max_seqlen_q, total_q, total_k, d, causal, scale, exp2_mode, tau, dtype,
+                            stream);
+}
+
+int attn_mx_scale_offsets(const int* cu_seqlens, int B, int total, int align, int* offsets, void* stream) {
+  if (B < 0 || total < 0) return fail(ATTN_E_SHAPE, "negative size (B=%d total=%d)", B, total);
+  if (align < 32 || align > 4096 || align % 32 != 0)
+    return fail(ATTN_E_SHAPE, "align=%d must be a multiple of 32 in [32, 4096]", align);
+  if ((long long)total / 32 + (long long)B * (align / 32 + 1) > 0x7FFFFFFFLL)
+    return fail(ATTN_E_SHAPE, "scale rows would overflow int32 (B=%d total=%d align=%d)", B, total, align);
+  if (!cu_seqlens || !offsets) return fail(ATTN_E_NULLPTR, "cu_seqlens and offsets must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) | reinterpret_cast<uintptr_t>(offsets)) & 3u)
+    return fail(ATTN_E_ALIGN, "cu_seqlens and offsets must be 4-byte aligned");
+  hipError_t e = attn::launch_scale_offsets(cu_seqlens, B, total, align, offsets, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+int attn_mx_scale_scatter(const uint8_t* src, const int* src_offsets, int src_rows, uint8_t* dst,
+                          const int* dst_offsets, int dst_rows, const int* cu_seqlens, int B, int total, int H, int d,
+                          void* stream) {
+  if (B < 0 || total < 0 || H < 0 || src_rows < 0 || dst_rows < 0)
+    return fail(ATTN_E_SHAPE, "negative size (B=%d total=%d H=%d src_rows=%d dst_rows=%d)", B, total, H, src_rows,
+                dst_rows);
+  if (d != 128) return fail(ATTN_E_HEADDIM, "MXFP8 supports d=128 (got %d)", d);
+  if (B == 0 || H == 0 || dst_rows == 0) return ATTN_OK;
+  if ((long long)std::max(src_rows, dst_rows) * H * (d / 32) > 0x7FFFFFFFLL)
+    return fail(ATTN_E_SHAPE, "scale tensors must stay under 2 GiB (rows %d/%d, H=%d)", src_rows, dst_rows, H);
+  if (!src || !src_offsets || !dst || !dst_offsets || !cu_seqlens)
+    return fail(ATTN_E_NULLPTR, "src, src_offsets, dst, dst_offsets and cu_seqlens must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) |
+       reinterpret_cast<uintptr_t>(src_offsets) | reinterpret_cast<uintptr_t>(dst_offsets) |
+       reinterpret_cast<uintptr_t>(cu_seqlens)) & 3u)
+    return fail(ATTN_E_ALIGN, "scale, offset and cu_seqlens pointers must be 4-byte aligned");
+  hipError_t e = attn::launch_scale_scatter(src, src_offsets, src_rows, dst, dst_offsets, dst_rows, cu_seqlens, B,
+                                            total, H * (d / 32), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
 }
 
 int attn_exp2(const float* x, float* y, long n, int exp2_mode, void* stream) {

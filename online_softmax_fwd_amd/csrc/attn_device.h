@@ -111,6 +111,44 @@ __device__ __forceinline__ Slice slice_of(int bh, int H, int d, int Nq, int Nk, 
   return s;
 }
 
+// E8M0 scales of slice (b, h), one byte per 32x32 block of rows x d. Dense
+// tensors are [B, H, N/32, d/32]. Packed batches address scales apart from
+// the data ("Quantization along both axes and jagged tensors" on the MXFP8
+// page: the FP8 data stays compact, only the scale tensors follow a layout
+// of their own): scales are [rows, H, d/32] with sequence b's 32-row blocks
+// starting at scale row off[b], so sequences may start at padded scale rows
+// while their data rows are packed. Block r of the slice holds the scales
+// of its rows 32r .. 32r+31; a sequence's last block may be partial. The
+// offsets are clamped to [0, rows] and blocks past rows read as absent, so
+// inconsistent offsets never move a read outside the scale tensor.
+struct ScaleSlice {
+  size_t qbase, kbase;  // byte offset of block 0 (K and V share a layout)
+  int qblocks, kblocks; // blocks present
+  uint32_t stride;      // bytes between consecutive blocks of the slice
+};
+__device__ __forceinline__ ScaleSlice scale_slice_of(int bh, int H, int d, int Nq, int Nk, const int* off_q,
+                                                     const int* off_k, int rows_q, int rows_k) {
+  ScaleSlice s;
+  const int w = d / 32;
+  const int nqb = (Nq + 31) / 32, nkb = (Nk + 31) / 32;
+  if (off_q == nullptr) {
+    s.qbase = (size_t)bh * nqb * w;
+    s.kbase = (size_t)bh * nkb * w;
+    s.qblocks = nqb;
+    s.kblocks = nkb;
+    s.stride = w;
+  } else {
+    const int b = bh / H, h = bh - b * H;
+    const int q0 = min(max(off_q[b], 0), rows_q), k0 = min(max(off_k[b], 0), rows_k);
+    s.qbase = ((size_t)q0 * H + h) * w;
+    s.kbase = ((size_t)k0 * H + h) * w;
+    s.qblocks = min(nqb, rows_q - q0);
+    s.kblocks = min(nkb, rows_k - k0);
+    s.stride = (uint32_t)(H * w);
+  }
+  return s;
+}
+
 // Causal query tiles differ in length: tile qt of a head needs its first
 // qt+1 tiles' worth of keys. When the heads split evenly over the 8 XCDs, XCD
 // x takes the heads bh = x (mod 8), all of whose tiles therefore share that

@@ -122,12 +122,19 @@ __device__ __forceinline__ uint32_t e8m0_of(float amax) {
 enum { kPBlock = 0, kPFixedE4M3 = 1, kPFixedE5M2 = 2 };
 constexpr int kMaxOffset = 8;
 
-template <bool CAUSAL, int EMU16, int PMODE>
+// PACKED: a batch of sequences packed token-major ([total, H, d] data,
+// [scale rows, H, d/32] scales at per-sequence scale offsets); lengths need
+// not be multiples of 32, so row validity is per lane and the last 32-key
+// block of a sequence may be partial (its keys past the end are masked and
+// read as zero).
+template <bool CAUSAL, int EMU16, int PMODE, bool PACKED>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
 void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
                       const uint8_t* __restrict__ QS, const uint8_t* __restrict__ KS, const uint8_t* __restrict__ VS,
                       __bf16* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats, int H,
-                      int Nq, int Nk, int n_qt, float c, float tau, int bottom_right) {
+                      int Nq_dense, int Nk_dense, int n_qt, float c, float tau, int bottom_right,
+                      const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k,
+                      const int* __restrict__ soff_q, const int* __restrict__ soff_k, int srows_q, int srows_k) {
   __shared__ __attribute__((aligned(1024))) char kb0[kTile];
   __shared__ __attribute__((aligned(1024))) char kb1[kTile];
   __shared__ __attribute__((aligned(1024))) char vb0[kTile];
@@ -149,10 +156,16 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + l32;
-  const bool wave_rows = qw0 < Nq;  // Nq is a multiple of 32: a wave's rows are all valid or all past the end
-  const size_t qbase = (size_t)bh * Nq * kD;
-  const size_t kbase = (size_t)bh * Nk * kD;
-  const int nqb = Nq / 32, nkb = Nk / 32;
+  const Slice sl = slice_of(bh, H, kD, Nq_dense, Nk_dense, PACKED ? cu_q : nullptr, cu_k, total_q, total_k);
+  const int Nq = sl.Nq, Nk = sl.Nk;
+  if (PACKED && q0 >= Nq) return;  // a query tile past this sequence's end
+  const ScaleSlice sc =
+      scale_slice_of(bh, H, kD, Nq, Nk, PACKED ? soff_q : nullptr, soff_k, srows_q, srows_k);
+  const bool wave_rows = qw0 < Nq;  // wave-uniform: the wave has rows to compute
+  const bool row_ok = qi < Nq;      // this lane's row (dense sizes are multiples of 32: equal to wave_rows)
+  const size_t qbase = sl.qbase, kbase = sl.kbase;
+  const int rs = PACKED ? sl.rs : kD;  // elements (= bytes of Q, K, V) between consecutive rows
+  const uint32_t tile_bytes = (uint32_t)kBN * rs;
 
   // ---- per-lane constants --------------------------------------------------
   const int krow = key_of_row(l32);
@@ -176,10 +189,10 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   for (int i = 0; i < kLoads; ++i) {
     const int pos = 64 * (wave + kWaves * i) + lane;
     const int r = pos / kCH, p = pos % kCH;
-    kld[i] = r * kRB + 16 * (p ^ swz_k(r));
-    vld[i] = r * kRB + 16 * (p ^ swz_v(r));
+    kld[i] = r * rs + 16 * (p ^ swz_k(r));
+    vld[i] = r * rs + 16 * (p ^ swz_v(r));
   }
-  const int nrec = Nk * kRB;
+  const int nrec = Nk * rs;
   const u32x4 rk = raw_buffer_rsrc(K + kbase, (uint32_t)nrec);
   const u32x4 rv = raw_buffer_rsrc(V + kbase, (uint32_t)nrec);
 
@@ -187,14 +200,14 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   i32x8 qf[2];
   uint32_t qsc = 0x7F7F7F7Fu;
   {
-    const uint8_t* qp = Q + qbase + (size_t)(wave_rows ? qi : 0) * kD + 16 * hh;
+    const uint8_t* qp = Q + qbase + (size_t)(row_ok ? qi : 0) * rs + 16 * hh;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const u32x4 lo = wave_rows ? *(const u32x4*)(qp + 64 * s) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 hi = wave_rows ? *(const u32x4*)(qp + 64 * s + 32) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 lo = row_ok ? *(const u32x4*)(qp + 64 * s) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 hi = row_ok ? *(const u32x4*)(qp + 64 * s + 32) : u32x4{0u, 0u, 0u, 0u};
       qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
-    if (wave_rows) qsc = *(const uint32_t*)(QS + ((size_t)bh * nqb + qw0 / 32) * 4);
+    if (wave_rows && qw0 / 32 < sc.qblocks) qsc = *(const uint32_t*)(QS + sc.qbase + (size_t)(qw0 / 32) * sc.stride);
   }
   // byte 2s of (qsc >> 8h) is the scale of d block 2s + h: op_sel picks byte 2s
   const int qscale = (int)(qsc >> (8 * hh));
@@ -214,22 +227,22 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int slot = 1024 * (wave + kWaves * i);
-      dma16(rk, kd + slot, kld[i] + (uint32_t)t * kTile);
-      dma16(rv, vd + slot, vld[i] + (uint32_t)t * kTile);
+      dma16(rk, kd + slot, kld[i] + (uint32_t)t * tile_bytes);
+      dma16(rv, vd + slot, vld[i] + (uint32_t)t * tile_bytes);
     }
   };
 
-  auto scale_word = [&](const uint8_t* base, int blk, int nblk) __attribute__((always_inline)) -> uint32_t {
-    return blk < nblk ? *(const uint32_t*)(base + (size_t)blk * 4) : 0x7F7F7F7Fu;
+  auto scale_word = [&](const uint8_t* base, int blk) __attribute__((always_inline)) -> uint32_t {
+    return blk < sc.kblocks ? *(const uint32_t*)(base + (size_t)blk * sc.stride) : 0x7F7F7F7Fu;
   };
 
   auto compute = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
     const int k0 = t * kBN;
     if ((CAUSAL && k0 > qw0 + 31 + diag) || !wave_rows) return;  // wave-uniform: nothing to add
-    const uint8_t* ksb = KS + (size_t)bh * nkb * 4;
-    const uint8_t* vsb = VS + (size_t)bh * nkb * 4;
-    const uint32_t kw0 = scale_word(ksb, 2 * t, nkb), kw1 = scale_word(ksb, 2 * t + 1, nkb);
-    const uint32_t vw0 = scale_word(vsb, 2 * t, nkb), vw1 = scale_word(vsb, 2 * t + 1, nkb);
+    const uint8_t* ksb = KS + sc.kbase;
+    const uint8_t* vsb = VS + sc.kbase;
+    const uint32_t kw0 = scale_word(ksb, 2 * t), kw1 = scale_word(ksb, 2 * t + 1);
+    const uint32_t vw0 = scale_word(vsb, 2 * t), vw1 = scale_word(vsb, 2 * t + 1);
     const int kscale[2] = {(int)(kw0 >> (8 * hh)), (int)(kw1 >> (8 * hh))};
     const int vscale = (int)(hh ? vw1 : vw0);  // lane half h supplies key block 2t + h; op_sel picks d block
 
@@ -271,7 +284,7 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
     const bool commit = seen && !(acc >= -tau);
     const float alpha = commit ? exp2_hw(acc) : 1.0f;
     if (stats) {
-      const bool step = seen && (m_run > kNegInf) && hh == 0;
+      const bool step = seen && (m_run > kNegInf) && hh == 0 && row_ok;
       const unsigned long long bs = __builtin_amdgcn_ballot_w64(step);
       const unsigned long long br = __builtin_amdgcn_ballot_w64(step && commit);
       cnt[0] += __builtin_popcountll(bs);
@@ -362,8 +375,8 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
 
   const float l_tot = pl_sum_halves(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that saw no key: O = 0, LSE = -inf
-  if (wave_rows) {
-    __bf16* op = O + qbase + (size_t)qi * kD + 4 * hh;
+  if (row_ok) {
+    __bf16* op = O + qbase + (size_t)qi * rs + 4 * hh;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -373,7 +386,7 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
         for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[db][4 * g + r] * inv);
         *(bf16x4*)(op + 32 * db + 8 * g) = w;
       }
-    if (hh == 0) LSE[(size_t)bh * Nq + qi] = (m_run * c + __builtin_log2f(l_tot)) * 0.693147180559945309f;
+    if (hh == 0) LSE[sl.lse + qi] = (m_run * c + __builtin_log2f(l_tot)) * 0.693147180559945309f;
   }
   if (stats && lane == 0) {
 #pragma unroll
@@ -381,14 +394,21 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   }
 }
 
-template <bool CAUSAL, int EMU16, int PMODE>
-hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+template <bool CAUSAL, int EMU16, int PMODE, bool PACKED>
+hipError_t launch_k(const FwdArgs& a, hipStream_t stream) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
   const long long grid = (long long)a.B * a.H * n_qt;
-  hipLaunchKernelGGL((fwd_mxfp8_kernel<CAUSAL, EMU16, PMODE>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_scale, a.k_scale, a.v_scale,
-                     (__bf16*)a.o, a.lse, a.stats, a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.bottom_right);
+  hipLaunchKernelGGL((fwd_mxfp8_kernel<CAUSAL, EMU16, PMODE, PACKED>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     stream, (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_scale, a.k_scale,
+                     a.v_scale, (__bf16*)a.o, a.lse, a.stats, a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau,
+                     a.bottom_right, a.cu_q, a.cu_k, a.total_q, a.total_k, a.scale_off_q, a.scale_off_k,
+                     a.scale_rows_q, a.scale_rows_k);
   return hipGetLastError();
+}
+
+template <bool CAUSAL, int EMU16, int PMODE>
+hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+  return a.cu_q ? launch_k<CAUSAL, EMU16, PMODE, true>(a, stream) : launch_k<CAUSAL, EMU16, PMODE, false>(a, stream);
 }
 
 template <bool CAUSAL, int PMODE>

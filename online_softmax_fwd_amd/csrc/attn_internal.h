@@ -23,6 +23,9 @@ struct FwdArgs {
   const int* cu_q;          // packed variable-length batch: sequence starts (B+1 entries), else nullptr
   const int* cu_k;
   int total_q, total_k;     // rows of the packed Q and K/V
+  const int* scale_off_q;   // packed MXFP8: first scale row of each sequence (B+1 entries)
+  const int* scale_off_k;
+  int scale_rows_q, scale_rows_k;  // rows of the packed scale tensors
   float scale_log2;         // scale * log2(e)
   float tau;                // lagging-max threshold, log2 units
   int emu16;                // software-exp2 share of P, in 16ths (0 = all hardware)
@@ -34,6 +37,12 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 // p_mode: 0 = P scaled per 32-key block, 1 = fixed 2^8 scale with E4M3 P,
 // 2 = fixed 2^8 scale with E5M2 P
 hipError_t launch_fwd_mxfp8(const FwdArgs& a, int p_mode, hipStream_t stream);
+// Packed MXFP8 scale layouts: first scale row of each sequence for a given
+// row alignment, and the copy of compact scale rows into another layout.
+hipError_t launch_scale_offsets(const int* cu, int B, int total, int align, int* off, hipStream_t stream);
+hipError_t launch_scale_scatter(const uint8_t* src, const int* src_off, int src_rows, uint8_t* dst,
+                                const int* dst_off, int dst_rows, const int* cu, int B, int total, int row_bytes,
+                                hipStream_t stream);
 hipError_t launch_exp2(const float* x, float* y, long n, int emulated, hipStream_t stream);
 
 // Emulated shares (in 16ths) that have a compiled kernel instance.

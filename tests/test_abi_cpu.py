@@ -29,7 +29,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert names == sorted(["attn_exp2", "attn_fwd", "attn_fwd_ex", "attn_fwd_stats", "attn_fwd_varlen",
-                            "attn_last_error", "attn_mix_sixteenths"])
+                            "attn_fwd_varlen_ex", "attn_last_error", "attn_mix_sixteenths",
+                            "attn_mx_scale_offsets", "attn_mx_scale_scatter"])
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {lib._name}").read()
@@ -165,3 +166,70 @@ def test_varlen_validation_errors(lib, kw, code):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(maxq=0), dict(tq=0, maxq=0)])
 def test_varlen_nothing_to_do(lib, kw):
     assert _varlen(lib, Q=None, K=None, V=None, O=None, LSE=None, cq=None, ck=None, **kw) == 0
+
+
+def _varlen_ex(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, qs=FAKE, ks=FAKE, vs=FAKE, cq=FAKE, ck=FAKE, sq=FAKE,
+             sk=FAKE, rq=10, rk=12, B=2, H=4, maxq=100, tq=150, tk=170, d=128, causal=0, scale=0.088, mode=0,
+             tau=0.0, dtype=2)
+    a.update(kw)
+    return lib.attn_fwd_varlen_ex(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["qs"], a["ks"], a["vs"], a["cq"],
+                                  a["ck"], a["sq"], a["sk"], a["rq"], a["rk"], a["B"], a["H"], a["maxq"], a["tq"],
+                                  a["tk"], a["d"], a["causal"], a["scale"], a["mode"], a["tau"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), -4),
+    (dict(d=64), -3),                 # MXFP8 is d = 128 only
+    (dict(rq=-1), -2),
+    (dict(qs=None), -1),
+    (dict(vs=None), -1),
+    (dict(sk=None), -1),
+    (dict(ks=FAKE + 2), -8),          # scale and offset pointers 4-byte aligned
+    (dict(sq=FAKE + 1), -8),
+    (dict(tau=1.0, dtype=3), -6),     # fixed-scale E4M3 P: 8 + tau < log2(448)
+    (dict(maxq=200), -2),
+    (dict(dtype=1, d=96), -3),        # bf16 keeps its own checks
+    (dict(dtype=1, cq=None), -1),
+])
+def test_varlen_ex_validation_errors(lib, kw, code):
+    assert _varlen_ex(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+def test_varlen_ex_ignores_scales_for_bf16(lib):
+    # bf16 with NULL scale arguments passes validation; nothing to do (B = 0)
+    assert _varlen_ex(lib, dtype=1, qs=None, ks=None, vs=None, sq=None, sk=None, rq=-1, rk=-1, B=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(total=-1), -2), (dict(align=48), -2), (dict(align=0), -2), (dict(align=8192), -2),
+    (dict(cu=None), -1), (dict(off=None), -1), (dict(off=FAKE + 2), -8),
+    (dict(B=1 << 28, align=4096), -2),       # row count could overflow int32
+])
+def test_mx_scale_offsets_validation(lib, kw, code):
+    a = dict(cu=FAKE, B=3, total=100, align=128, off=FAKE)
+    a.update(kw)
+    assert lib.attn_mx_scale_offsets(a["cu"], a["B"], a["total"], a["align"], a["off"], None) == code
+    assert lib.attn_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(src_rows=-1), -2), (dict(d=64), -3), (dict(src=None), -1), (dict(cu=None), -1),
+    (dict(dst=FAKE + 2), -8), (dict(dst_off=FAKE + 1), -8), (dict(dst_rows=1 << 28, H=4), -2),
+])
+def test_mx_scale_scatter_validation(lib, kw, code):
+    a = dict(src=FAKE, src_off=FAKE, src_rows=8, dst=FAKE, dst_off=FAKE, dst_rows=16, cu=FAKE, B=3, total=100,
+             H=2, d=128)
+    a.update(kw)
+    assert lib.attn_mx_scale_scatter(a["src"], a["src_off"], a["src_rows"], a["dst"], a["dst_off"], a["dst_rows"],
+                                     a["cu"], a["B"], a["total"], a["H"], a["d"], None) == code
+    assert lib.attn_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(dst_rows=0)])
+def test_mx_scale_scatter_nothing_to_do(lib, kw):
+    a = dict(B=3, H=2, dst_rows=16)
+    a.update(kw)
+    assert lib.attn_mx_scale_scatter(None, None, 8, None, None, a["dst_rows"], None, a["B"], 100, a["H"], 128,
+                                     None) == 0

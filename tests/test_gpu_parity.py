@@ -10,7 +10,7 @@ import math
 import numpy as np
 import pytest
 
-from attn_inputs import WORKLOADS, make_inputs
+from attn_inputs import WORKLOADS, make_inputs, make_packed_inputs
 from oracle import attention_f64, attention_rows_f64, blockwise_f64, ex2_emu_deg3
 
 from _gpu import TOL_LSE, TOL_O, announce, attn_module, host64, run_fwd, to_device
@@ -462,3 +462,130 @@ def test_varlen_parity(attn, name, causal):
         _compare_with_empty_rows(torch.from_numpy(oh[q0:q0 + nq].transpose(1, 0, 2)[None].copy()),
                                  torch.from_numpy(lh[:, q0:q0 + nq][None].copy()), o_ref, lse_ref, w.dtype,
                                  f"{what} sequence {b} (Nq={nq}, Nk={nk})")
+
+
+# ---------------------------------------------------------------------------
+# Packed MXFP8 batches with split-addressed scales (attn_fwd_varlen_ex): FP8
+# data packed token-major, scale rows of each sequence at offsets of their
+# own. MX blocks start at each sequence's first token, so tails are partial
+# blocks. Each sequence against the oracle on the dequantised values.
+# ---------------------------------------------------------------------------
+def _mx_packed_device(x):
+    import torch
+    dev = torch.device("cuda", 0)
+    t = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(dev)
+         for n in ("q", "k", "v", "qs", "ks", "vs", "cu_q", "cu_k", "sq_off", "sk_off")}
+    return t
+
+
+def _seen(nq, nk, causal):
+    """Boolean [nq, nk]: keys each query row attends to."""
+    diag = {False: None, "top_left": 0, "bottom_right": nk - nq}[causal]
+    if diag is None:
+        return np.ones((nq, nk), dtype=bool)
+    return np.arange(nk)[None, :] <= np.arange(nq)[:, None] + diag
+
+
+@pytest.mark.parametrize("fp8_p", ["block", "e4m3", "e5m2"])
+@pytest.mark.parametrize("causal", [False, "top_left", "bottom_right"])
+def test_varlen_mxfp8_parity(attn, fp8_p, causal):
+    import torch
+    what = f"mxfp8 packed P={fp8_p} causal={causal}"
+    announce(what)
+    H = 3
+    x = make_packed_inputs(MX, VARLEN_Q, VARLEN_K, H, seed=4343)
+    t = _mx_packed_device(x)
+    o, lse = attn.fwd_varlen(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], max(VARLEN_Q), causal=causal,
+                             exp2_mode="hw", tau=0.0, q_scale=t["qs"], k_scale=t["ks"], v_scale=t["vs"],
+                             scale_offsets_q=t["sq_off"], scale_offsets_k=t["sk_off"], fp8_p=fp8_p)
+    oh, lh = host64(o), host64(lse)
+    p_rel = 2.0 ** -3 if fp8_p == "e5m2" else E4M3_REL
+    for b, (nq, nk) in enumerate(zip(VARLEN_Q, VARLEN_K)):
+        if nq == 0:
+            continue
+        q0, k0 = x["cu_q"][b], x["cu_k"][b]
+        seq = f"{what} sequence {b} (Nq={nq}, Nk={nk})"
+        if nk == 0:
+            assert np.all(oh[q0:q0 + nq] == 0.0) and np.all(lh[:, q0:q0 + nq] == -np.inf), seq
+            continue
+        qs = x["q64"][q0:q0 + nq].transpose(1, 0, 2)[None]
+        ks = x["k64"][k0:k0 + nk].transpose(1, 0, 2)[None]
+        vs = x["v64"][k0:k0 + nk].transpose(1, 0, 2)[None]
+        o_ref, lse_ref = attention_f64(qs, ks, vs, causal=causal)
+        seen = _seen(nq, nk, causal)
+        o_got = oh[q0:q0 + nq].transpose(1, 0, 2)[None]
+        l_got = lh[:, q0:q0 + nq][None]
+        if fp8_p == "block":
+            # per row: 2^-4 * max |v| over the keys it sees (the dense MXFP8 tests' bound)
+            tol_rows = np.zeros(lse_ref.shape)
+            for h in range(H):
+                for i in range(nq):
+                    if seen[i].any():
+                        tol_rows[0, h, i] = E4M3_REL * np.abs(vs[0, h][seen[i]]).max()
+            _compare_with_empty_rows(torch.from_numpy(o_got.copy()), torch.from_numpy(l_got.copy()), o_ref,
+                                     lse_ref, "mxfp8", seq, tol_rows)
+        else:
+            # the fixed-scale P bound of test_mxfp8_fixed_p_scale_parity, per element
+            empty = ~np.isfinite(lse_ref)
+            assert np.array_equal(~np.isfinite(l_got), empty) and np.all(o_got[empty] == 0.0), seq
+            for h in range(H):
+                s = np.where(seen, (qs[0, h] @ ks[0, h].T) / np.sqrt(qs.shape[-1]), -np.inf)
+                full = ~empty[0, h]
+                wgt = np.exp(s[full] - lse_ref[0, h][full][:, None])
+                bound = p_rel * (wgt @ np.abs(vs[0, h])) + 2.0 ** -8 * np.abs(o_ref[0, h][full]) + 1e-4
+                d_o = np.abs(o_got[0, h][full] - o_ref[0, h][full])
+                d_l = np.abs(l_got[0, h][full] - lse_ref[0, h][full])
+                assert np.all(np.isfinite(d_o)) and np.all(d_o <= bound), (seq, h, (d_o / bound).max())
+                assert d_l.max(initial=0.0) <= TOL_LSE, (seq, h)
+
+
+def _padded_offsets_host(cu, align):
+    lens = np.diff(cu.astype(np.int64))
+    return np.concatenate([[0], np.cumsum((lens + align - 1) // align * (align // 32))]).astype(np.int32)
+
+
+@pytest.mark.parametrize("align", [32, 64, 128, 256])
+def test_mx_scale_offsets_match_definition(attn, align):
+    """Device offsets against the definition: an exclusive prefix sum of
+    ceil(len / align) * align / 32 (bit-exact); also over more sequences than
+    one scan chunk, with empty sequences."""
+    import torch
+    rng = np.random.default_rng(align)
+    for lens in (VARLEN_Q, VARLEN_K, list(rng.integers(0, 300, size=1000)), [0] * 257, []):
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        got = attn.mx_scale_offsets(torch.from_numpy(cu).cuda(), int(cu[-1]), align).cpu().numpy()
+        assert np.array_equal(got, _padded_offsets_host(cu, align)), (align, len(lens))
+
+
+def test_mx_scale_scatter_and_padded_layout(attn):
+    """Compact scales scattered into 128-aligned rows equal the host layout
+    (bit-exact, padding rows 127), and attention on the padded layout returns
+    exactly what it returns on the compact one (the kernel reads the same
+    scale bytes either way)."""
+    import torch
+    H = 3
+    x = make_packed_inputs(MX, VARLEN_Q, VARLEN_K, H, seed=4444)
+    t = _mx_packed_device(x)
+    padded = {}
+    for side, cu, src, off in (("q", x["cu_q"], x["qs"], x["sq_off"]), ("k", x["cu_k"], x["ks"], x["sk_off"]),
+                               ("v", x["cu_k"], x["vs"], x["sk_off"])):
+        poff = _padded_offsets_host(cu, 128)
+        want = np.full((int(poff[-1]), H, 4), 127, dtype=np.uint8)
+        for b in range(len(cu) - 1):
+            n = (int(cu[b + 1] - cu[b]) + 31) // 32
+            want[poff[b]:poff[b] + n] = src[off[b]:off[b] + n]
+        dev_poff = attn.mx_scale_offsets(t["cu_" + ("q" if side == "q" else "k")], int(cu[-1]), 128)
+        got = attn.mx_scale_scatter(t[side + "s"], t["s" + ("q" if side == "q" else "k") + "_off"], dev_poff,
+                                    int(poff[-1]), t["cu_" + ("q" if side == "q" else "k")], int(cu[-1]))
+        assert np.array_equal(got.cpu().numpy(), want), side
+        padded[side] = (got, dev_poff)
+    for causal in (False, "bottom_right"):
+        kw = dict(causal=causal, exp2_mode="hw", tau=0.0)
+        o1, l1 = attn.fwd_varlen(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], max(VARLEN_Q), q_scale=t["qs"],
+                                 k_scale=t["ks"], v_scale=t["vs"], scale_offsets_q=t["sq_off"],
+                                 scale_offsets_k=t["sk_off"], **kw)
+        o2, l2 = attn.fwd_varlen(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], max(VARLEN_Q),
+                                 q_scale=padded["q"][0], k_scale=padded["k"][0], v_scale=padded["v"][0],
+                                 scale_offsets_q=padded["q"][1], scale_offsets_k=padded["k"][1], **kw)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), causal
+        assert torch.equal(l1, l2) or np.array_equal(host64(l1), host64(l2)), causal
