@@ -1,4 +1,4 @@
-"""Oracle for the attention forward pass: plain, slow, float64 CPU code.
+"""Oracle for the attention forward and backward passes: plain, slow, float64 CPU code.
 
 TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call,
 link or execute anything under ``oracle/``; only the test suite, the smoke
@@ -10,6 +10,8 @@ none of the attention arithmetic.
 Contents
   attention_f64        one-shot safe softmax attention, the plain definition
   attention_rows_f64   the same for a chosen subset of query rows
+  attention_bwd_f64    the backward pass: dQ, dK, dV (and D) in closed form
+  attention_loss_f64   sum(O * dO), the scalar those are the gradients of
   blockwise_f64        the streaming recurrence with the lagging-max rule
                        (used only to pin the recurrence and its rescale
                        counts; never the parity reference)
@@ -26,8 +28,9 @@ brute force at 50 digits, library routines that differ from the ones used
 here, and the numbers the pages print. No function is "parity unpinned".
 """
 from .attention import attention_f64, attention_rows_f64, blockwise_f64
+from .attention_bwd import attention_bwd_f64, attention_loss_f64
 from .ex2_emu import ex2_emu_deg3, build_ex2_emu
 from .p_cast import lagging_max_p_cast_f64, rel_l2, round_to_format
 
-__all__ = ["attention_f64", "attention_rows_f64", "blockwise_f64",
+__all__ = ["attention_f64", "attention_rows_f64", "blockwise_f64", "attention_bwd_f64", "attention_loss_f64",
            "ex2_emu_deg3", "build_ex2_emu", "lagging_max_p_cast_f64", "rel_l2", "round_to_format"]
