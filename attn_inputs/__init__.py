@@ -22,7 +22,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "make_inputs", "mx_quantize_packed", "mx_compact_offsets", "bf16_bits", "bf16_bits_to_f32",
+    "Workload", "WORKLOADS", "make_inputs", "make_grad_output", "mx_quantize_packed", "mx_compact_offsets", "bf16_bits", "bf16_bits_to_f32",
     "e4m3_decode_table", "e4m3_encode", "e8m0_for_amax", "mx_quantize",
     "mx_dequantize", "make_score_inputs", "make_packed_inputs",
 ]
@@ -233,6 +233,17 @@ def make_score_inputs(sigma: float, seed: int, rows: int = 256, keys: int = 8192
     scores = rng.standard_normal((rows, keys)) * sigma
     v = rng.standard_normal((keys, d))
     return scores, v
+
+
+def make_grad_output(shape, seed: int, dtype: str = "bf16"):
+    """dO for the backward pass: float32 standard normals of `shape` from
+    default_rng(seed), as bf16 bit patterns (dtype "bf16") or float32, with
+    the exact float64 values the kernel receives."""
+    g = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+    if dtype == "bf16":
+        bits = bf16_bits(g)
+        return bits, bf16_bits_to_f32(bits).astype(np.float64)
+    return g, g.astype(np.float64)
 
 
 def make_packed_inputs(w: Workload | str, q_lens, k_lens, H: int, seed: int):

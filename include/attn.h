@@ -265,6 +265,51 @@ int attn_mx_scale_scatter(const uint8_t* src, const int* src_offsets, int src_ro
                           int total, int H, int d, void* stream);
 
 /*
+ * attn_bwd_workspace_bytes -- bytes of float32 workspace attn_bwd needs:
+ * 8 * B * H * Nq (two floats per query row); -1 for negative sizes.
+ */
+long long attn_bwd_workspace_bytes(int B, int H, int Nq);
+
+/*
+ * attn_bwd -- attention backward: dQ, dK, dV from dO and the forward pass's
+ * O and LSE.
+ *
+ * Source: "PyTorch FlashAttention-4 adds MXFP8 block-scaled forward and
+ * backward for Blackwell", section "TMEM allocation and scale factor
+ * placement" (five products; dK and dV accumulate over the whole pass), and
+ * "Lecture 2 -- Online Softmax and Numerical Correctness", section "Use it in
+ * the real stack" (the forward pass's LSE rebuilds P, which is what makes the
+ * backward pass cheap). With P = exp(scale * Q K^T - LSE) (masked as in
+ * attn_fwd): dV = P^T dO, dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D),
+ * dQ = scale * dS K, dK = scale * dS^T Q.
+ *
+ *   Q, O, dO       device bf16 [B, H, Nq, d];  K, V: device bf16 [B, H, Nk, d]
+ *   LSE            device float32 [B, H, Nq], natural log, as attn_fwd writes it
+ *                  (-inf for a row that saw no key: that row gets dQ = 0 and
+ *                  adds nothing to dK, dV)
+ *   dQ             device bf16 [B, H, Nq, d] (written)
+ *   dK, dV         device bf16 [B, H, Nk, d] (written; keys no query sees get 0)
+ *   workspace      device, >= attn_bwd_workspace_bytes(B, H, Nq) bytes, owned
+ *                  by the caller; holds per-row LSE*log2(e) and D between the
+ *                  three kernels of one call (contents on entry are ignored)
+ *   workspace_bytes  its size
+ *   d              64 or 128;  causal 0, 1 (top-left) or 2 (bottom-right)
+ *   scale          the forward pass's scale (> 0, finite)
+ *   dtype          ATTN_BF16
+ *   stream         hipStream_t (NULL = the null stream); asynchronous
+ * Tensors with no elements may be NULL (Nq = 0: Q, O, dO, LSE, dQ, workspace;
+ * Nk = 0: K, V, dK, dV). All pointers 16-byte aligned. Errors: ATTN_E_DTYPE,
+ * ATTN_E_SHAPE (negative or too large sizes, workspace too small, causal not
+ * 0..2), ATTN_E_HEADDIM, ATTN_E_SCALE, ATTN_E_NULLPTR, ATTN_E_ALIGN,
+ * ATTN_E_HIP; every check happens before any launch. Calls that share a
+ * workspace must not overlap.
+ */
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
+             long long workspace_bytes, int B, int H, int Nq, int Nk, int d, int causal,
+             float scale, int dtype, void* stream);
+
+/*
  * attn_fwd_stats -- attn_fwd_ex that also counts lagging-max rescale events.
  *
  *   stats     device uint64 [4], accumulated into (the caller zeroes it):

@@ -21,7 +21,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_varlen", "fwd_stats", "mx_scale_offsets", "mx_scale_scatter", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
+__all__ = ["fwd", "fwd_varlen", "fwd_stats", "bwd", "mx_scale_offsets", "mx_scale_scatter", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
            "ATTN_F32", "ATTN_BF16", "ATTN_MXFP8_E4M3", "ATTN_MXFP8_E4M3_PFIX_E4M3", "ATTN_MXFP8_E4M3_PFIX_E5M2",
            "EXP2_MODES", "STATUS"]
 
@@ -67,6 +67,10 @@ def load_library():
     lib.attn_fwd_varlen.restype = ci
     lib.attn_fwd_varlen_ex.argtypes = [vp] * 12 + [ci] * 9 + [cf, ci, cf, ci, vp]
     lib.attn_fwd_varlen_ex.restype = ci
+    lib.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_longlong
+    lib.attn_bwd.argtypes = [vp] * 10 + [ctypes.c_longlong, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.attn_bwd.restype = ci
     lib.attn_mx_scale_offsets.argtypes = [vp, ci, ci, ci, vp, vp]
     lib.attn_mx_scale_offsets.restype = ci
     lib.attn_mx_scale_scatter.argtypes = [vp, vp, ci, vp, vp, ci, vp, ci, ci, ci, ci, vp]
@@ -242,6 +246,39 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal=Fa
                                   _causal(causal), scale, _mode(exp2_mode), float(tau), dtype,
                                   _stream_ptr(stream, q.device)))
     return out, lse
+
+
+def bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Attention backward through attn_bwd: (dQ, dK, dV) from dO and the
+    forward pass's O and LSE. q, o, do: bfloat16 [B, H, Nq, d]; k, v:
+    bfloat16 [B, H, Nk, d]; lse: float32 [B, H, Nq]. The float32 workspace
+    (8*B*H*Nq bytes) is allocated here unless given."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape or o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if not lse.is_cuda or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, Nq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} has the wrong shape, dtype or layout")
+    nbytes = int(lib.attn_bwd_workspace_bytes(B, H, Nq))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), B, H, Nq, Nk, d, _causal(causal), scale,
+                        ATTN_BF16, _stream_ptr(stream, q.device)))
+    return dq, dk, dv
 
 
 def mx_scale_offsets(cu_seqlens, total: int, align: int = 32, out=None, stream=None):

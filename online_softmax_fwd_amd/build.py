@@ -29,6 +29,7 @@ SOURCES = [
     "attn_fwd_f32.hip",
     "attn_fwd_mxfp8.hip",
     "attn_mx_layout.hip",
+    "attn_bwd_bf16.hip",
 ]
 
 COMMON_FLAGS = [

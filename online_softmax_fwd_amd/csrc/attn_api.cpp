@@ -320,6 +320,64 @@ int attn_mx_scale_scatter(const uint8_t* src, const int* src_offsets, int src_ro
   return ATTN_OK;
 }
 
+long long attn_bwd_workspace_bytes(int B, int H, int Nq) {
+  if (B < 0 || H < 0 || Nq < 0) return -1;
+  return 8LL * B * H * Nq;
+}
+
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
+             void* dK, void* dV, float* workspace, long long workspace_bytes, int B, int H, int Nq, int Nk, int d,
+             int causal, float scale, int dtype, void* stream) {
+  if (dtype != ATTN_BF16) return fail(ATTN_E_DTYPE, "attn_bwd takes ATTN_BF16 (got dtype %d)", dtype);
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(ATTN_E_SHAPE, "negative size (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
+  if (d != 64 && d != 128) return fail(ATTN_E_HEADDIM, "attn_bwd supports d=64 and d=128 (got %d)", d);
+  if (causal < 0 || causal > 2) return fail(ATTN_E_SHAPE, "causal=%d is not 0, 1 or 2", causal);
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(ATTN_E_SCALE, "scale=%g must be finite and > 0", scale);
+  if ((long long)B * H == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
+  const long long n_t = (std::max(Nq, Nk) + 127) / 128;
+  if ((long long)B * H * n_t > 0x7FFFFFFFLL || Nq > (1 << 30) || Nk > (1 << 30))
+    return fail(ATTN_E_SHAPE, "sizes too large (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
+  // one (batch, head) slice of Q, K, V or dO is addressed with 32-bit byte
+  // offsets, up to one tile past the end
+  if (((long long)std::max(Nq, Nk) + 256) * d * 2 > 0x7FFFFFFFLL)
+    return fail(ATTN_E_SHAPE, "one (batch, head) slice must stay under 2 GiB (Nq=%d Nk=%d d=%d)", Nq, Nk, d);
+  if (workspace_bytes < attn_bwd_workspace_bytes(B, H, Nq))
+    return fail(ATTN_E_SHAPE, "workspace of %lld bytes; attn_bwd_workspace_bytes gives %lld", workspace_bytes,
+                attn_bwd_workspace_bytes(B, H, Nq));
+  // tensors with no elements (Nq = 0: Q, O, dO, LSE, dQ, workspace; Nk = 0:
+  // K, V, dK, dV) are never touched and may be NULL
+  if (Nq > 0 && (!Q || !O || !dO || !LSE || !dQ || !workspace))
+    return fail(ATTN_E_NULLPTR, "Q, O, dO, LSE, dQ and workspace must be non-NULL");
+  if (Nk > 0 && (!K || !V || !dK || !dV)) return fail(ATTN_E_NULLPTR, "K, V, dK and dV must be non-NULL");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(LSE) ||
+      !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
+    return fail(ATTN_E_ALIGN, "every tensor and the workspace must be 16-byte aligned");
+  attn::BwdArgs a;
+  a.q = Q;
+  a.k = K;
+  a.v = V;
+  a.o = O;
+  a.d_o = dO;
+  a.lse = LSE;
+  a.d_q = dQ;
+  a.d_k = dK;
+  a.d_v = dV;
+  a.ws = workspace;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.causal = causal != 0;
+  a.bottom_right = causal == 2;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
+  hipError_t e = attn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
 int attn_exp2(const float* x, float* y, long n, int exp2_mode, void* stream) {
   if (exp2_mode != ATTN_EXP2_HW && exp2_mode != ATTN_EXP2_EMU)
     return fail(ATTN_E_EXP2MODE, "attn_exp2 takes ATTN_EXP2_HW (0) or ATTN_EXP2_EMU (1), got %d", exp2_mode);

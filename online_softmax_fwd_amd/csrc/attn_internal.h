@@ -31,9 +31,29 @@ struct FwdArgs {
   int emu16;                // software-exp2 share of P, in 16ths (0 = all hardware)
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* d_o;
+  const float* lse;
+  void* d_q;
+  void* d_k;
+  void* d_v;
+  float* ws;                // 2 floats per query row: LSE * log2(e), D = rowsum(dO * O)
+  int B, H, Nq, Nk, d;
+  int causal;               // 0 or 1
+  int bottom_right;
+  float scale;
+  float scale_log2;         // scale * log2(e)
+};
+
 // Each returns hipSuccess or the launch error; none synchronises.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+// prep pass, dK/dV kernel, dQ kernel, in that order on `stream`
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 // p_mode: 0 = P scaled per 32-key block, 1 = fixed 2^8 scale with E4M3 P,
 // 2 = fixed 2^8 scale with E5M2 P
 hipError_t launch_fwd_mxfp8(const FwdArgs& a, int p_mode, hipStream_t stream);

@@ -23,12 +23,13 @@ def lib():
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "attn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(attn_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|long long|const char\*)\s+(attn_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert names == sorted(["attn_exp2", "attn_fwd", "attn_fwd_ex", "attn_fwd_stats", "attn_fwd_varlen",
+    assert names == sorted(["attn_bwd", "attn_bwd_workspace_bytes", "attn_exp2", "attn_fwd", "attn_fwd_ex",
+                            "attn_fwd_stats", "attn_fwd_varlen",
                             "attn_fwd_varlen_ex", "attn_last_error", "attn_mix_sixteenths",
                             "attn_mx_scale_offsets", "attn_mx_scale_scatter"])
     for n in names:
@@ -233,3 +234,37 @@ def test_mx_scale_scatter_nothing_to_do(lib, kw):
     a.update(kw)
     assert lib.attn_mx_scale_scatter(None, None, 8, None, None, a["dst_rows"], None, a["B"], 100, a["H"], 128,
                                      None) == 0
+
+
+def _bwd(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, LSE=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE, ws=FAKE, wsb=1 << 20,
+             B=2, H=3, Nq=100, Nk=120, d=128, causal=0, scale=0.088, dtype=1)
+    a.update(kw)
+    return lib.attn_bwd(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"], a["dK"], a["dV"], a["ws"],
+                        a["wsb"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.attn_bwd_workspace_bytes(2, 3, 100) == 8 * 2 * 3 * 100
+    assert lib.attn_bwd_workspace_bytes(0, 3, 100) == 0
+    assert lib.attn_bwd_workspace_bytes(-1, 3, 100) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), -4), (dict(dtype=2), -4),
+    (dict(B=-1), -2), (dict(Nk=-1), -2), (dict(causal=3), -2), (dict(causal=-1), -2),
+    (dict(d=96), -3), (dict(scale=0.0), -7), (dict(scale=float("nan")), -7),
+    (dict(wsb=8 * 2 * 3 * 100 - 4), -2),          # workspace one float short
+    (dict(Q=None), -1), (dict(dK=None), -1), (dict(ws=None), -1), (dict(LSE=None), -1),
+    (dict(dV=FAKE + 8), -8), (dict(ws=FAKE + 4), -8),
+    (dict(Nq=1 << 24, Nk=1 << 24), -2),           # a slice of 2 GiB or more
+])
+def test_bwd_validation_errors(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Nq=0, Nk=0)])
+def test_bwd_nothing_to_do(lib, kw):
+    assert _bwd(lib, Q=None, K=None, V=None, O=None, dO=None, LSE=None, dQ=None, dK=None, dV=None, ws=None,
+                wsb=0, **kw) == 0
