@@ -19,6 +19,11 @@ Prints ONE JSON line. Besides the contract fields it carries
                 (null when no counter run covers these kernel sources)
   rescale       lagging-max rescale counts per mode, from one counting launch
                 (attn_fwd_stats) outside the timed region
+  backward      bf16 workloads: the backward pass (attn_bwd) on the same
+                inputs with the forward's O and LSE and a seeded dO, timed
+                after the forward's timed region (HIP events per call on the
+                launch stream); FLOPs counted as 2.5 x the forward's (the five
+                products S, dP, dV, dK, dQ); not part of "value"
   cpu_baseline  the float64 oracle timed on a bounded sample of the same
                 workload on the host cores (rank 0, N=1 only)
 """
@@ -78,6 +83,9 @@ def parse():
     p.add_argument("--fp8-p", default="block", choices=["block", "e4m3", "e5m2"],
                    help="MXFP8 workloads: P scaled per 32-key block, or times 2^8 with one fixed scale as E4M3 or E5M2")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-bwd", action="store_true", help="skip the backward-pass section")
+    p.add_argument("--bwd-steps", type=int, default=50)
+    p.add_argument("--bwd-warmup", type=int, default=50)
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (HBM counter calibration)")
     return p.parse_args()
@@ -120,6 +128,48 @@ def cpu_baseline(w, causal_modes, flop_budget=1.2e12):
                   f"softmax (it forms the full S even when causal; FLOPs counted as for the GPU); {dt:.1f} s",
         "seconds": round(dt, 2),
     }
+
+
+def fwd_kernel_name(w, causal: bool) -> str:
+    """The kernel a launch of this workload runs (the bf16 path has a
+    streaming kernel for d = 64 and causal d = 128, a ping-pong kernel for
+    non-causal d = 128)."""
+    if w.dtype == "bf16":
+        return "fwd_bf16_stream_kernel" if (w.d == 64 or causal) else "fwd_bf16_kernel"
+    return f"fwd_{w.dtype}_kernel"
+
+
+def bench_backward(attn, w, q, k, v, outs, stream, args):
+    import numpy as np
+    import torch
+    from attn_inputs import make_grad_output
+    bits, _ = make_grad_output((w.B, w.H, w.Nq, w.d), w.seed + 1)
+    do = torch.from_numpy(bits.view(np.int16)).to(q.device).view(torch.bfloat16)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(2 * w.B * w.H * w.Nq, dtype=torch.float32, device=q.device)
+    res = {}
+    for c in w.causal:
+        o, lse = outs[c]
+
+        def call():
+            attn.bwd(q, k, v, o, do, lse, causal=c, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+        for _ in range(args.bwd_warmup):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.bwd_steps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        fl = 2.5 * flops_of(w, c)
+        res["causal" if c else "noncausal"] = {
+            "ms_mean": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "pct_of_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[w.dtype], 2)}
+    res["flops_note"] = "2.5 x the forward's FLOPs per call; kernels: bwd_prep, bwd_dkdv, bwd_dq"
+    return res
 
 
 def main():
@@ -243,7 +293,7 @@ def main():
         "per_mode": per_mode,
         "roofline": {
             "bound": "mfma",
-            "kernel": f"fwd_{w.dtype}_kernel (d={w.d}, {'causal' if dom else 'non-causal'})",
+            "kernel": f"{fwd_kernel_name(w, dom)} (d={w.d}, {'causal' if dom else 'non-causal'})",
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": "TFLOP/s",
@@ -260,6 +310,8 @@ def main():
             "row_tile_steps": st[0], "row_rescales": st[1], "wave_tile_steps": st[2], "wave_rescales": st[3],
             "row_frac": round(st[1] / max(st[0], 1), 6), "wave_frac": round(st[3] / max(st[2], 1), 6)}
     result["rescale"] = rescale
+    if w.dtype == "bf16" and not args.no_bwd:
+        result["backward"] = bench_backward(attn, w, q, k, v, outs, stream, args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, w.causal)
     print(json.dumps(result), flush=True)
