@@ -17,6 +17,8 @@ Contents
                        counts; never the parity reference)
   ex2_emu_deg3         float32 CPU model of the degree-3 software exp2
                        (C, built with gcc; see ex2_emu.c)
+  ex2_emu              the same with the degree-4 or degree-5 polynomial
+  fit_ex2_poly         the fit that produced the degree-4/5 coefficients
   round_to_format      cast to bf16 / OCP E4M3 / OCP E5M2 (nearest-even,
                        saturating)
   lagging_max_p_cast_f64
@@ -29,8 +31,9 @@ here, and the numbers the pages print. No function is "parity unpinned".
 """
 from .attention import attention_f64, attention_rows_f64, blockwise_f64
 from .attention_bwd import attention_bwd_f64, attention_loss_f64
-from .ex2_emu import ex2_emu_deg3, build_ex2_emu
+from .ex2_emu import ex2_emu, ex2_emu_deg3, build_ex2_emu
+from .fit_ex2_poly import fit_ex2_poly
 from .p_cast import lagging_max_p_cast_f64, rel_l2, round_to_format
 
 __all__ = ["attention_f64", "attention_rows_f64", "blockwise_f64", "attention_bwd_f64", "attention_loss_f64",
-           "ex2_emu_deg3", "build_ex2_emu", "lagging_max_p_cast_f64", "rel_l2", "round_to_format"]
+           "ex2_emu", "ex2_emu_deg3", "build_ex2_emu", "fit_ex2_poly", "lagging_max_p_cast_f64", "rel_l2", "round_to_format"]

@@ -1,7 +1,8 @@
 /*
  * Test infrastructure, not product code: a float32 CPU model of the
- * degree-3 software exp2 used by the attention forward path. Only the test
- * suite, the smoke check and the bench's CPU-baseline leg load it.
+ * software exp2 used by the attention path (degree 3, and the degree-4 and
+ * degree-5 variants). Only the test suite, the smoke check and the bench's
+ * CPU-baseline leg load it.
  *
  * Source: "FlashAttention-4's Softmax Tricks: A Degree-3 exp2 on the FMA
  * Pipe, and a Lagging Max That Saturated FP8", section "The emulated exp2"
@@ -25,6 +26,15 @@ static const float kP0 = 1.0f;
 static const float kP1 = 0.695146143436431884765625f;
 static const float kP2 = 0.227564394474029541015625f;
 static const float kP3 = 0.077119089663028717041015625f;
+
+/* Degree-4 and degree-5 coefficients, not printed on the pages (their error
+ * rows are): fitted the same way, relative-error minimax with constant term
+ * 1, rounded to float32 (oracle/fit_ex2_poly.py). */
+static const float kQ4[5] = {1.0f, 0.693044841289520263671875f, 0.2412802278995513916015625f,
+                             0.05224247276782989501953125f, 0.013426683843135833740234375f};
+static const float kQ5[6] = {1.0f, 0.693151295185089111328125f, 0.2401644885540008544921875f,
+                             0.055799908936023712158203125f, 0.009017030708491802215576171875f,
+                             0.001867130049504339694976806640625f};
 
 static uint32_t bits_of(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
 static float float_of(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
@@ -53,4 +63,22 @@ float ex2_emu_deg3_one(float x)
 void ex2_emu_deg3(const float* x, float* y, long n)
 {
     for (long i = 0; i < n; ++i) y[i] = ex2_emu_deg3_one(x[i]);
+}
+
+/* The same steps with the degree-4 or degree-5 polynomial (Horner, one fmaf
+ * per step, highest coefficient first). Other degrees leave y untouched. */
+void ex2_emu_poly(const float* x, float* y, long n, int degree)
+{
+    const float* c = degree == 4 ? kQ4 : degree == 5 ? kQ5 : 0;
+    if (degree == 3) { ex2_emu_deg3(x, y, n); return; }
+    if (!c) return;
+    for (long i = 0; i < n; ++i) {
+        float xc = fmaxf(x[i], -127.0f);
+        const float magic = 12582912.0f;
+        float x_rounded = floorf(xc) + magic;
+        float x_frac = xc - (x_rounded - magic);
+        float p = c[degree];
+        for (int k = degree - 1; k >= 0; --k) p = fmaf(p, x_frac, c[k]);
+        y[i] = float_of((bits_of(x_rounded) << 23) + bits_of(p));
+    }
 }

@@ -1,4 +1,4 @@
-"""ctypes loader for the C model of the degree-3 software exp2 (ex2_emu.c).
+"""ctypes loader for the C model of the software exp2 (ex2_emu.c; degrees 3, 4, 5).
 
 Test infrastructure only (see the package docstring). The shared object is
 built with gcc next to this file; ``build_ex2_emu()`` always rebuilds it,
@@ -34,6 +34,8 @@ def _lib():
         h = ctypes.CDLL(_LIB)
         h.ex2_emu_deg3.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long]
         h.ex2_emu_deg3.restype = None
+        h.ex2_emu_poly.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_int]
+        h.ex2_emu_poly.restype = None
         _handle = h
     return _handle
 
@@ -43,4 +45,15 @@ def ex2_emu_deg3(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     y = np.empty_like(x)
     _lib().ex2_emu_deg3(x.ctypes.data, y.ctypes.data, x.size)
+    return y
+
+
+def ex2_emu(x: np.ndarray, degree: int = 3) -> np.ndarray:
+    """Emulated exp2 of a float32 array with the degree-3, -4 or -5
+    polynomial (float32 result)."""
+    if degree not in (3, 4, 5):
+        raise ValueError(f"degree {degree} is not 3, 4 or 5")
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty_like(x)
+    _lib().ex2_emu_poly(x.ctypes.data, y.ctypes.data, x.size, degree)
     return y
