@@ -96,12 +96,20 @@ enum {
  *                  tuning table keyed by (dtype, d, causal)
  *   ATTN_EXP2_MIX_BASE + k (k = 0..16)  the same with exactly k of every 16 P
  *                  emulated (for tuning sweeps)
+ *   ATTN_EXP2_EMU4, ATTN_EXP2_EMU5  every P through the software exp2 with a
+ *                  degree-4 / degree-5 polynomial (same section's error table:
+ *                  max relative error 3.05e-6 / 1.44e-7 against 8.77e-5 at degree
+ *                  3; the page prints no coefficients, the library's are a fit of
+ *                  the same kind: relative-error minimax, p0 = 1, float32).
+ *                  ATTN_F32 and ATTN_BF16 only (ATTN_E_EXP2MODE for MXFP8).
  * The rescale factor and the LSE logarithm always use the hardware units.
  */
 enum {
   ATTN_EXP2_HW = 0,
   ATTN_EXP2_EMU = 1,
   ATTN_EXP2_MIX = 2,
+  ATTN_EXP2_EMU4 = 3,
+  ATTN_EXP2_EMU5 = 4,
   ATTN_EXP2_MIX_BASE = 16
 };
 
@@ -329,7 +337,8 @@ int attn_fwd_stats(const void* Q, const void* K, const void* V, void* O, float* 
 
 /*
  * attn_exp2 -- y[i] = 2^x[i] through the same device exp2 the attention kernels
- * inline (ATTN_EXP2_HW or ATTN_EXP2_EMU; MIX is not a per-element mode here).
+ * inline (ATTN_EXP2_HW, ATTN_EXP2_EMU, ATTN_EXP2_EMU4 or ATTN_EXP2_EMU5; MIX is
+ * not a per-element mode here).
  *   x, y      device float32 [n]; may alias
  *   n         >= 0
  * The software exp2 is defined for x <= 127 and returns 0 for x <= -127 and -inf.

@@ -28,7 +28,7 @@ __all__ = ["fwd", "fwd_varlen", "fwd_stats", "bwd", "mx_scale_offsets", "mx_scal
 ATTN_F32, ATTN_BF16, ATTN_MXFP8_E4M3 = 0, 1, 2
 ATTN_MXFP8_E4M3_PFIX_E4M3, ATTN_MXFP8_E4M3_PFIX_E5M2 = 3, 4
 FP8_P = {"block": ATTN_MXFP8_E4M3, "e4m3": ATTN_MXFP8_E4M3_PFIX_E4M3, "e5m2": ATTN_MXFP8_E4M3_PFIX_E5M2}
-EXP2_MODES = {"hw": 0, "emu": 1, "mix": 2}
+EXP2_MODES = {"hw": 0, "emu": 1, "mix": 2, "emu4": 3, "emu5": 4}
 MIX_BASE = 16
 STATUS = {0: "ATTN_OK", -1: "ATTN_E_NULLPTR", -2: "ATTN_E_SHAPE", -3: "ATTN_E_HEADDIM", -4: "ATTN_E_DTYPE",
           -5: "ATTN_E_EXP2MODE", -6: "ATTN_E_TAU", -7: "ATTN_E_SCALE", -8: "ATTN_E_ALIGN", -9: "ATTN_E_HIP"}

@@ -82,12 +82,17 @@ int validate_common(int dtype, int d, int causal, float scale, int exp2_mode, fl
     *emu16 = 0;
   } else if (exp2_mode == ATTN_EXP2_EMU) {
     *emu16 = 16;
+  } else if (exp2_mode == ATTN_EXP2_EMU4 || exp2_mode == ATTN_EXP2_EMU5) {
+    if (is_mx(dtype))
+      return fail(ATTN_E_EXP2MODE, "exp2_mode=%d (degree-%d software exp2) is for ATTN_F32 and ATTN_BF16", exp2_mode,
+                  exp2_mode == ATTN_EXP2_EMU4 ? 4 : 5);
+    *emu16 = exp2_mode == ATTN_EXP2_EMU4 ? attn::kEmuDeg4Code : attn::kEmuDeg5Code;
   } else if (exp2_mode == ATTN_EXP2_MIX) {
     *emu16 = mix_table(dtype, d, causal != 0);
   } else if (exp2_mode >= ATTN_EXP2_MIX_BASE && exp2_mode <= ATTN_EXP2_MIX_BASE + 16) {
     *emu16 = exp2_mode - ATTN_EXP2_MIX_BASE;
   } else {
-    return fail(ATTN_E_EXP2MODE, "exp2_mode=%d is not HW (0), EMU (1), MIX (2) or MIX_BASE+k (16..32)",
+    return fail(ATTN_E_EXP2MODE, "exp2_mode=%d is not HW (0), EMU (1), MIX (2), EMU4 (3), EMU5 (4) or MIX_BASE+k (16..32)",
                 exp2_mode);
   }
   if (*emu16 < 0 || !attn::emu16_supported(*emu16))
@@ -379,14 +384,16 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
 }
 
 int attn_exp2(const float* x, float* y, long n, int exp2_mode, void* stream) {
-  if (exp2_mode != ATTN_EXP2_HW && exp2_mode != ATTN_EXP2_EMU)
-    return fail(ATTN_E_EXP2MODE, "attn_exp2 takes ATTN_EXP2_HW (0) or ATTN_EXP2_EMU (1), got %d", exp2_mode);
+  if (exp2_mode != ATTN_EXP2_HW && exp2_mode != ATTN_EXP2_EMU && exp2_mode != ATTN_EXP2_EMU4 &&
+      exp2_mode != ATTN_EXP2_EMU5)
+    return fail(ATTN_E_EXP2MODE, "attn_exp2 takes ATTN_EXP2_HW (0), EMU (1), EMU4 (3) or EMU5 (4), got %d", exp2_mode);
   if (n < 0) return fail(ATTN_E_SHAPE, "n=%ld is negative", n);
   if (n == 0) return ATTN_OK;
   if (!x || !y) return fail(ATTN_E_NULLPTR, "x and y must be non-NULL");
   if ((reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(y) & 3u))
     return fail(ATTN_E_ALIGN, "x and y must be 4-byte aligned");
-  hipError_t e = attn::launch_exp2(x, y, n, exp2_mode == ATTN_EXP2_EMU, static_cast<hipStream_t>(stream));
+  const int degree = exp2_mode == ATTN_EXP2_HW ? 0 : exp2_mode == ATTN_EXP2_EMU ? 3 : exp2_mode == ATTN_EXP2_EMU4 ? 4 : 5;
+  hipError_t e = attn::launch_exp2(x, y, n, degree, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
 }

@@ -32,21 +32,43 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float exp2_emu(float x) {
-  const float c1 = 0.695146143436431884765625f;
-  const float c2 = 0.227564394474029541015625f;
-  const float c3 = 0.077119089663028717041015625f;
+// The polynomial has degree DEG: 3 uses the coefficients the page prints;
+// 4 and 5 use the same kind of fit (relative-error minimax, p0 = 1, float32
+// coefficients), whose errors the page's table lists (3.05e-6 and 1.44e-7
+// maximum relative error against 8.77e-5 for degree 3).
+template <int DEG>
+__device__ __forceinline__ float exp2_emu_deg(float x) {
+  static_assert(DEG >= 3 && DEG <= 5, "degree");
   float xc = __builtin_fmaxf(x, -127.0f);
   float fr = __builtin_amdgcn_fractf(xc);
   int fl = (int)__builtin_floorf(xc);
-  float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c3, fr, c2), fr, c1), fr, 1.0f);
+  float p;
+  if (DEG == 3) {
+    p = __builtin_fmaf(0.077119089663028717041015625f, fr, 0.227564394474029541015625f);
+    p = __builtin_fmaf(p, fr, 0.695146143436431884765625f);
+  } else if (DEG == 4) {
+    p = __builtin_fmaf(0.013426683843135833740234375f, fr, 0.05224247276782989501953125f);
+    p = __builtin_fmaf(p, fr, 0.2412802278995513916015625f);
+    p = __builtin_fmaf(p, fr, 0.693044841289520263671875f);
+  } else {
+    p = __builtin_fmaf(0.001867130049504339694976806640625f, fr, 0.009017030708491802215576171875f);
+    p = __builtin_fmaf(p, fr, 0.055799908936023712158203125f);
+    p = __builtin_fmaf(p, fr, 0.2401644885540008544921875f);
+    p = __builtin_fmaf(p, fr, 0.693151295185089111328125f);
+  }
+  p = __builtin_fmaf(p, fr, 1.0f);
   return __builtin_bit_cast(float, ((uint32_t)fl << 23) + __builtin_bit_cast(uint32_t, p));
 }
+__device__ __forceinline__ float exp2_emu(float x) { return exp2_emu_deg<3>(x); }
 
 // The MIX policy: element j (0..15) of each lane's 16-score group goes through
-// the software path when j < EMU16.
+// the software path when j < EMU16. Two more codes select full emulation with
+// the higher-degree polynomials.
+constexpr int kEmuDeg4 = 17, kEmuDeg5 = 18;
 template <int EMU16>
 __device__ __forceinline__ float exp2_sel(float x, int j) {
+  if (EMU16 == kEmuDeg4) return exp2_emu_deg<4>(x);
+  if (EMU16 == kEmuDeg5) return exp2_emu_deg<5>(x);
   if (EMU16 >= 16) return exp2_emu(x);
   if (EMU16 <= 0) return exp2_hw(x);
   return (j < EMU16) ? exp2_emu(x) : exp2_hw(x);

@@ -7,24 +7,27 @@
 namespace attn {
 namespace {
 
-template <bool EMU>
+template <int DEG>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void exp2_kernel(const float* __restrict__ x, float* __restrict__ y, long n) {
   const long stride = (long)gridDim.x * blockDim.x;
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    y[i] = EMU ? exp2_emu(x[i]) : exp2_hw(x[i]);
+    y[i] = DEG == 0 ? exp2_hw(x[i]) : exp2_emu_deg<DEG == 0 ? 3 : DEG>(x[i]);
 }
 
 }  // namespace
 
-hipError_t launch_exp2(const float* x, float* y, long n, int emulated, hipStream_t stream) {
+hipError_t launch_exp2(const float* x, float* y, long n, int degree, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   long blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  if (emulated)
-    hipLaunchKernelGGL((exp2_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, x, y, n);
-  else
-    hipLaunchKernelGGL((exp2_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, x, y, n);
+  switch (degree) {
+    case 0: hipLaunchKernelGGL((exp2_kernel<0>), dim3((unsigned)blocks), dim3(256), 0, stream, x, y, n); break;
+    case 3: hipLaunchKernelGGL((exp2_kernel<3>), dim3((unsigned)blocks), dim3(256), 0, stream, x, y, n); break;
+    case 4: hipLaunchKernelGGL((exp2_kernel<4>), dim3((unsigned)blocks), dim3(256), 0, stream, x, y, n); break;
+    case 5: hipLaunchKernelGGL((exp2_kernel<5>), dim3((unsigned)blocks), dim3(256), 0, stream, x, y, n); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -692,6 +692,8 @@ hipError_t launch_mode(const FwdArgs& a, hipStream_t stream) {
     case 4: return launch<D, CAUSAL, 4>(a, stream);
     case 8: return launch<D, CAUSAL, 8>(a, stream);
     case 16: return launch<D, CAUSAL, 16>(a, stream);
+    case kEmuDeg4: return launch<D, CAUSAL, kEmuDeg4>(a, stream);
+    case kEmuDeg5: return launch<D, CAUSAL, kEmuDeg5>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -699,7 +701,8 @@ hipError_t launch_mode(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool emu16_supported(int emu16) {
-  return emu16 == 0 || emu16 == 1 || emu16 == 2 || emu16 == 3 || emu16 == 4 || emu16 == 8 || emu16 == 16;
+  return emu16 == 0 || emu16 == 1 || emu16 == 2 || emu16 == 3 || emu16 == 4 || emu16 == 8 || emu16 == 16 ||
+         emu16 == kEmuDeg4 || emu16 == kEmuDeg5;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {

@@ -244,6 +244,8 @@ hipError_t launch_mode(const FwdArgs& a, hipStream_t stream) {
     case 4: return launch<D, CAUSAL, 4>(a, stream);
     case 8: return launch<D, CAUSAL, 8>(a, stream);
     case 16: return launch<D, CAUSAL, 16>(a, stream);
+    case kEmuDeg4: return launch<D, CAUSAL, kEmuDeg4>(a, stream);
+    case kEmuDeg5: return launch<D, CAUSAL, kEmuDeg5>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -63,8 +63,12 @@ hipError_t launch_scale_offsets(const int* cu, int B, int total, int align, int*
 hipError_t launch_scale_scatter(const uint8_t* src, const int* src_off, int src_rows, uint8_t* dst,
                                 const int* dst_off, int dst_rows, const int* cu, int B, int total, int row_bytes,
                                 hipStream_t stream);
-hipError_t launch_exp2(const float* x, float* y, long n, int emulated, hipStream_t stream);
+// degree 0 = hardware exp2, 3..5 = the software exp2 with that polynomial
+hipError_t launch_exp2(const float* x, float* y, long n, int degree, hipStream_t stream);
 
+// Codes for full emulation with the degree-4 / degree-5 polynomial (the same
+// values as kEmuDeg4 / kEmuDeg5 in attn_device.h).
+constexpr int kEmuDeg4Code = 17, kEmuDeg5Code = 18;
 // Emulated shares (in 16ths) that have a compiled kernel instance.
 bool emu16_supported(int emu16);
 

@@ -66,7 +66,9 @@ def _call(lib, **kw):
     (dict(tau=-1.0), -6),
     (dict(tau=float("nan")), -6),
     (dict(tau=65.0), -6),
-    (dict(mode=3), -5),
+    (dict(mode=5), -5),
+    (dict(mode=3, dtype=2, qs=FAKE, ks=FAKE, vs=FAKE), -5),   # degree-4/5 software exp2 is f32/bf16 only
+    (dict(mode=4, dtype=4, qs=FAKE, ks=FAKE, vs=FAKE, tau=0.0), -5),
     (dict(mode=16 + 5), -5),          # no instance emulates 5/16
     (dict(mode=16 + 17), -5),
     (dict(Q=None), -1),
@@ -106,6 +108,9 @@ def test_exp2_validation(lib):
     assert lib.attn_exp2(None, None, 0, 1, None) == 0
     assert lib.attn_exp2(None, FAKE, 5, 1, None) == -1
     assert lib.attn_exp2(FAKE + 2, FAKE, 5, 1, None) == -8
+    assert lib.attn_exp2(None, None, 0, 3, None) == 0      # degree-4 and degree-5 software exp2
+    assert lib.attn_exp2(None, None, 0, 4, None) == 0
+    assert lib.attn_exp2(FAKE, FAKE, 10, 5, None) == -5
 
 
 def test_stats_validation(lib):
