@@ -45,7 +45,7 @@ constexpr int kPMaxOffset = 8;  // P scale exponent of the fixed-scale FP8 P dty
 // mode) are all fastest all-hardware. The float32 kernel follows the bf16
 // entries.
 int mix_table(int dtype, int d, int causal) {
-  if (d != 64 && d != 128) return -1;
+  if (d != 64 && d != 128 && !(dtype == ATTN_BF16 && (d == 192 || d == 256))) return -1;
   switch (dtype) {
     case ATTN_BF16:
     case ATTN_F32:
@@ -62,7 +62,9 @@ int mix_table(int dtype, int d, int causal) {
 int validate_common(int dtype, int d, int causal, float scale, int exp2_mode, float tau, int* emu16) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16 && !is_mx(dtype))
     return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32, ATTN_BF16 or one of the ATTN_MXFP8 codes", dtype);
-  if (d != 64 && d != 128) return fail(ATTN_E_HEADDIM, "head dim d=%d is not 64 or 128", d);
+  if (dtype == ATTN_BF16 ? (d != 64 && d != 128 && d != 192 && d != 256) : (d != 64 && d != 128))
+    return fail(ATTN_E_HEADDIM, "head dim d=%d is not supported for dtype %d (bf16: 64, 128, 192, 256; f32: 64, 128; "
+                "MXFP8: 128)", d, dtype);
   if (causal < 0 || causal > 2)
     return fail(ATTN_E_SHAPE, "causal=%d is not 0 (none), 1 (top-left) or 2 (bottom-right)", causal);
   if (!std::isfinite(scale) || !(scale > 0.0f))

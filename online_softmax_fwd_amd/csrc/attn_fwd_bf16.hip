@@ -65,18 +65,21 @@ struct Cfg {
   static constexpr int KB = BN / 32;          // 32-key MFMA blocks per tile
   static constexpr int LOADS = BN * CH / 64 / NW;  // wave-loads per wave per tensor per tile
   static_assert(LOADS >= 1 && LOADS * 64 * NW == BN * CH, "tile does not split evenly over the waves");
-  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(D == 64 || D == 128 || D == 192 || D == 256, "head dim");
 };
 
 // Swizzles (16-byte chunk position of logical chunk c in row r is c ^ f(r)).
 // K reads touch one chunk of 16 rows per 16-lane group: f_K makes those 16
 // rows land on 16 different bank groups. V transpose reads touch 4 chunks of
 // 8 rows per instruction: f_V spreads them so each bank is hit exactly twice
-// (512 bytes, the minimum of two passes).
+// (512 bytes, the minimum of two passes). Rows of 256 or 512 bytes start on
+// bank 0 (d = 128, 256); rows of 128 or 384 bytes alternate between bank 0 and
+// bank 32 (d = 64, 192), so there odd and even rows share XOR values. At
+// d = 192 (24 chunks) every XOR stays below 8, which keeps a chunk in its row.
 template <int D>
-__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int swz_k(int r) { return (D == 128 || D == 256) ? (r & 15) : ((r >> 1) & 7); }
 template <int D>
-__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+__device__ __forceinline__ int swz_v(int r) { return (D == 128 || D == 256) ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 
 
@@ -429,7 +432,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
 
 // ---------------------------------------------------------------------------
-// Streaming kernel: d = 64, and causal d = 128. Each wave owns 32 query rows
+// Streaming kernel: d = 64, 192 and 256, and causal d = 128. Each wave owns 32 query rows
 // and runs the S^T MFMAs, the softmax and the PV MFMAs of a key tile in
 // order, with no cross-wave phases; K and V tiles stream through two LDS
 // buffers shared by the workgroup. Several workgroups share a CU, so each
@@ -444,9 +447,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // d = 128: 4 waves x 32-key tiles, three workgroups per CU (~157 VGPRs, 32 KB
 // of LDS each); used for causal launches, where the 128-row workgroups also
 // balance the triangle's uneven work better than 256-row ones.
+// d = 192, 256: 4 waves x 32-key tiles, two workgroups per CU (the O
+// accumulators alone take d/2 VGPRs, Q another d/4; 48 / 64 KB of LDS each).
 template <int D>
 struct StreamCfg : Cfg<D, D == 64 ? 64 : 32, D == 64 ? 8 : 4> {
-  static constexpr int WAVES_PER_SIMD = D == 64 ? 4 : 3;
+  static constexpr int WAVES_PER_SIMD = D == 64 ? 4 : D == 128 ? 3 : 2;
 };
 
 template <int D, bool CAUSAL, int EMU16, bool PACKED>
@@ -489,15 +494,21 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
   const uint32_t tile_bytes = (uint32_t)BN * rsb;
   const int diag = bottom_right ? Nk - Nq : 0;  // causal: key j hidden from query i when j > i + diag
 
-  uint32_t koff[D / 16], voff[D / 32], kld[C::LOADS], vld[C::LOADS];
+  // The swizzles XOR only the low 3 (d = 64, 192) or 4 (d = 128, 256) chunk
+  // bits, so the read offsets repeat every KP 16-wide d steps and every VP
+  // 32-wide d blocks, shifted by a whole number of 128 / 256 bytes: only the
+  // first period lives in registers, the shift is an instruction immediate.
+  constexpr int KP = (D == 128 || D == 256) ? 8 : 4, VP = KP / 2;
+  constexpr int NKO = D / 16 < KP ? D / 16 : KP, NVO = D / 32 < VP ? D / 32 : VP;
+  uint32_t koff[NKO], voff[NVO], kld[C::LOADS], vld[C::LOADS];
   {
     const int krow = key_of_row(l32);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) koff[s] = krow * C::RB + 16 * ((2 * s + hh) ^ swz_k<D>(krow));
+    for (int s = 0; s < NKO; ++s) koff[s] = krow * C::RB + 16 * ((2 * s + hh) ^ swz_k<D>(krow));
     const int L = lane & 15, gidx = (lane >> 4) & 1;
     const int vr = 8 * hh + (L >> 2);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < NVO; ++db) {
       const int cch = 4 * db + 2 * gidx + ((L & 3) >> 1);
       voff[db] = vr * C::RB + 16 * (cch ^ swz_v<D>(vr)) + 8 * (L & 1);
     }
@@ -550,7 +561,7 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 a = *(const bf16x8*)(ks + kb * 32 * C::RB + koff[st]);
+        const bf16x8 a = *(const bf16x8*)(ks + kb * 32 * C::RB + koff[st % KP] + (st / KP) * 32 * KP);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? floatx16{} : s[kb], 0, 0, 0);
       }
     }
@@ -602,7 +613,7 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const char* vp = vs + voff[db] + (kb * 32 + 16 * cc) * C::RB;
+          const char* vp = vs + voff[db % VP] + (db / VP) * 64 * VP + (kb * 32 + 16 * cc) * C::RB;
           const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp));
           const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp + 4 * C::RB));
           const bf16x8 a = __builtin_bit_cast(
@@ -676,7 +687,7 @@ hipError_t launch_k(const FwdArgs& a, hipStream_t stream) {
 
 template <int D, bool CAUSAL, int EMU16>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  if constexpr (D == 64 || CAUSAL)
+  if constexpr (D != 128 || CAUSAL)
     return a.cu_q ? launch_stream<D, CAUSAL, EMU16, true>(a, stream) : launch_stream<D, CAUSAL, EMU16, false>(a, stream);
   else
     return a.cu_q ? launch_k<D, CAUSAL, EMU16, true>(a, stream) : launch_k<D, CAUSAL, EMU16, false>(a, stream);
@@ -708,6 +719,8 @@ bool emu16_supported(int emu16) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 128) return a.causal ? launch_mode<128, true>(a, stream) : launch_mode<128, false>(a, stream);
   if (a.d == 64) return a.causal ? launch_mode<64, true>(a, stream) : launch_mode<64, false>(a, stream);
+  if (a.d == 192) return a.causal ? launch_mode<192, true>(a, stream) : launch_mode<192, false>(a, stream);
+  if (a.d == 256) return a.causal ? launch_mode<256, true>(a, stream) : launch_mode<256, false>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -56,7 +56,9 @@ def _call(lib, **kw):
     (dict(B=-1), -2),
     (dict(Nk=0), -2),
     (dict(d=96), -3),
-    (dict(d=256), -3),
+    (dict(d=256, dtype=0), -3),       # f32: d 64, 128
+    (dict(d=192, dtype=2, qs=FAKE, ks=FAKE, vs=FAKE), -3),   # MXFP8: d 128
+    (dict(d=320), -3),
     (dict(causal=3), -2),
     (dict(causal=-1), -2),
     (dict(scale=0.0), -7),
@@ -126,6 +128,9 @@ def test_mix_table(lib):
             for causal in (0, 1):
                 k = lib.attn_mix_sixteenths(dtype, d, causal)
                 assert 0 <= k <= 16
+    for d in (192, 256):                       # bf16 only
+        assert 0 <= lib.attn_mix_sixteenths(1, d, 1) <= 16
+        assert lib.attn_mix_sixteenths(0, d, 1) < 0
     assert lib.attn_mix_sixteenths(1, 96, 0) < 0
     assert lib.attn_mix_sixteenths(9, 128, 0) < 0
 

@@ -389,7 +389,7 @@ def _compare_with_empty_rows(o, lse, o_ref, lse_ref, dtype, what, tol_rows=None)
 
 
 @pytest.mark.parametrize("name", ["bf16_b4h16_n4096_d128", "bf16_b2h32_n8192_d64_causal_spiky",
-                                  "fp32_b1h1_n128_d64"])
+                                  "fp32_b1h1_n128_d64", "bf16_b4h16_n4096_d192", "bf16_b4h16_n4096_d256"])
 @pytest.mark.parametrize("nq,nk", [(100, 333), (333, 100), (600, 100), (1, 300), (300, 1), (256, 256)])
 def test_bottom_right_parity(attn, name, nq, nk):
     w = WORKLOADS[name]
@@ -431,7 +431,7 @@ VARLEN_K = [333, 50, 129, 10, 0, 512, 700]
 
 
 @pytest.mark.parametrize("name", ["bf16_b4h16_n4096_d128", "bf16_b2h32_n8192_d64_causal_spiky",
-                                  "fp32_b1h1_n128_d64"])
+                                  "fp32_b1h1_n128_d64", "bf16_b4h16_n4096_d192", "bf16_b4h16_n4096_d256"])
 @pytest.mark.parametrize("causal", [False, "top_left", "bottom_right"])
 def test_varlen_parity(attn, name, causal):
     import torch
