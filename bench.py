@@ -19,7 +19,7 @@ Prints ONE JSON line. Besides the contract fields it carries
                 (null when no counter run covers these kernel sources)
   rescale       lagging-max rescale counts per mode, from one counting launch
                 (attn_fwd_stats) outside the timed region
-  backward      bf16 workloads: the backward pass (attn_bwd) on the same
+  backward      bf16 workloads at d 64 and 128: the backward pass (attn_bwd) on the same
                 inputs with the forward's O and LSE and a seeded dO, timed
                 after the forward's timed region (HIP events per call on the
                 launch stream); FLOPs counted as 2.5 x the forward's (the five
@@ -46,14 +46,15 @@ DEFAULT_WORKLOAD = "bf16_b4h16_n4096_d128"
 # HBM traffic of one non-causal launch of the default workload, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch, --calib-copy-mib 256). Calibrated on a plain 256 MiB device copy in
-# the same runs: FETCH_SIZE read 131088.8 KiB for 262144 KiB moved (x2.0),
+# the same runs: FETCH_SIZE read 131088.4 KiB for 262144 KiB moved (x2.0),
 # WRITE_SIZE read 262144 KiB (x1.0). Valid only for the kernel sources it was
 # taken on (first 16 hex digits of their SHA-256); any edit turns it off.
 TRAFFIC = {
     "workload": "bf16_b4h16_n4096_d128",
-    "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "be484923ac20791d",
-                "online_softmax_fwd_amd/csrc/attn_device.h": "ac8149acc05ef8a2"},
-    "fetch_kib_raw": 98458.7, "fetch_scale": 2.0,
+    "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "358baa1b6f946245",
+                "online_softmax_fwd_amd/csrc/attn_device.h": "0505e9cf734434e7",
+                "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "f8ea718687adf92d"},
+    "fetch_kib_raw": 98456.8, "fetch_scale": 2.0,
     "write_kib_raw": 66560.0, "write_scale": 1.0,
 }
 
@@ -135,7 +136,7 @@ def fwd_kernel_name(w, causal: bool) -> str:
     streaming kernel for d = 64 and causal d = 128, a ping-pong kernel for
     non-causal d = 128)."""
     if w.dtype == "bf16":
-        return "fwd_bf16_stream_kernel" if (w.d == 64 or causal) else "fwd_bf16_kernel"
+        return "fwd_bf16_stream_kernel" if (w.d != 128 or causal) else "fwd_bf16_kernel"
     return f"fwd_{w.dtype}_kernel"
 
 
@@ -310,7 +311,7 @@ def main():
             "row_tile_steps": st[0], "row_rescales": st[1], "wave_tile_steps": st[2], "wave_rescales": st[3],
             "row_frac": round(st[1] / max(st[0], 1), 6), "wave_frac": round(st[3] / max(st[2], 1), 6)}
     result["rescale"] = rescale
-    if w.dtype == "bf16" and not args.no_bwd:
+    if w.dtype == "bf16" and w.d in (64, 128) and not args.no_bwd:    # the backward pass's head dims
         result["backward"] = bench_backward(attn, w, q, k, v, outs, stream, args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, w.causal)
