@@ -318,6 +318,54 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
              float scale, int dtype, void* stream);
 
 /*
+ * attn_bwd_ex -- attn_bwd for ATTN_BF16 and ATTN_MXFP8_E4M3.
+ *
+ * Source: as attn_bwd, and "PyTorch FlashAttention-4 adds MXFP8 block-scaled
+ * forward and backward for Blackwell", section "Quantization along both axes
+ * and jagged tensors": the backward products reduce along both axes, so Q, K,
+ * V and dO are quantised in square 32x32 blocks (one e4m3 payload serves a
+ * product and its transpose), and dS likewise, so that dK and dQ consume the
+ * same representation.
+ *
+ * ATTN_MXFP8_E4M3 (d = 128; Nq, Nk multiples of 32):
+ *   Q, K, V, dO    e4m3 bytes [B, H, N, 128]
+ *   q_scale, k_scale, v_scale, do_scale
+ *                  E8M0 bytes [B, H, N/32, 4], one per 32x32 block (those of
+ *                  attn_fwd_ex for Q, K, V; attn_mx_quantize writes dO's)
+ *   O              bf16 [B, H, Nq, 128] as attn_fwd_ex wrote it; LSE float32
+ *   dQ, dK, dV     bf16 (written)
+ * Inside, P is stored times 2^8 with one fixed scale (P <= 1: the LSE is
+ * exact) and dS with one E8M0 byte per 32x32 block from its amax.
+ * Other arguments and errors as attn_bwd; additionally ATTN_E_SHAPE for MXFP8
+ * sizes that are not multiples of 32, ATTN_E_NULLPTR / ATTN_E_ALIGN for
+ * missing or unaligned (4-byte) scale pointers. For ATTN_BF16 the scale
+ * pointers are ignored.
+ */
+int attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
+                long long workspace_bytes, int B, int H, int Nq, int Nk, int d, int causal,
+                float scale, int dtype, const uint8_t* q_scale, const uint8_t* k_scale,
+                const uint8_t* v_scale, const uint8_t* do_scale, void* stream);
+
+/*
+ * attn_mx_quantize -- bf16 [rows, 128] to e4m3 [rows, 128] with one E8M0 byte
+ * per square 32x32 block ([rows/32, 4]), the layout attn_fwd_ex and
+ * attn_bwd_ex read (pass rows = B*H*N with N a multiple of 32).
+ *
+ * Source: "PyTorch FlashAttention-4 adds MXFP8 block-scaled forward and
+ * backward for Blackwell", section "Quantization along both axes and jagged
+ * tensors" (square 32x32 blocks for Q, K and dO), with the scale rule of its
+ * section "Softmax conversion and unroll-KV" (from the amax's exponent and
+ * mantissa bits): the byte is that of the smallest power of two X with
+ * amax / X <= 448 (X = 1 for an all-zero block); elements are divided by X
+ * and rounded to the nearest e4m3 value (ties to even).
+ *   x       device bf16, 16-byte aligned;  q: device bytes, 16-byte aligned
+ *   scale   device bytes;  rows: multiple of 32;  d: 128
+ * Errors: ATTN_E_HEADDIM, ATTN_E_SHAPE, ATTN_E_NULLPTR, ATTN_E_ALIGN, ATTN_E_HIP.
+ */
+int attn_mx_quantize(const void* x, uint8_t* q, uint8_t* scale, long long rows, int d, void* stream);
+
+/*
  * attn_fwd_stats -- attn_fwd_ex that also counts lagging-max rescale events.
  *
  *   stats     device uint64 [4], accumulated into (the caller zeroes it):

@@ -21,7 +21,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_varlen", "fwd_stats", "bwd", "mx_scale_offsets", "mx_scale_scatter", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
+__all__ = ["fwd", "fwd_varlen", "fwd_stats", "bwd", "mx_quantize", "mx_scale_offsets", "mx_scale_scatter", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
            "ATTN_F32", "ATTN_BF16", "ATTN_MXFP8_E4M3", "ATTN_MXFP8_E4M3_PFIX_E4M3", "ATTN_MXFP8_E4M3_PFIX_E5M2",
            "EXP2_MODES", "STATUS"]
 
@@ -71,6 +71,10 @@ def load_library():
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_longlong
     lib.attn_bwd.argtypes = [vp] * 10 + [ctypes.c_longlong, ci, ci, ci, ci, ci, ci, cf, ci, vp]
     lib.attn_bwd.restype = ci
+    lib.attn_bwd_ex.argtypes = [vp] * 10 + [ctypes.c_longlong, ci, ci, ci, ci, ci, ci, cf, ci, vp, vp, vp, vp, vp]
+    lib.attn_bwd_ex.restype = ci
+    lib.attn_mx_quantize.argtypes = [vp, vp, vp, ctypes.c_longlong, ci, vp]
+    lib.attn_mx_quantize.restype = ci
     lib.attn_mx_scale_offsets.argtypes = [vp, ci, ci, ci, vp, vp]
     lib.attn_mx_scale_offsets.restype = ci
     lib.attn_mx_scale_scatter.argtypes = [vp, vp, ci, vp, vp, ci, vp, ci, ci, ci, ci, vp]
@@ -248,25 +252,39 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal=Fa
     return out, lse
 
 
-def bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Attention backward through attn_bwd: (dQ, dK, dV) from dO and the
-    forward pass's O and LSE. q, o, do: bfloat16 [B, H, Nq, d]; k, v:
-    bfloat16 [B, H, Nk, d]; lse: float32 [B, H, Nq]. The float32 workspace
-    (8*B*H*Nq bytes) is allocated here unless given."""
+def bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
+        q_scale=None, k_scale=None, v_scale=None, do_scale=None):
+    """Attention backward through attn_bwd_ex: (dQ, dK, dV) from dO and the
+    forward pass's O and LSE. bf16: q, o, do bfloat16 [B, H, Nq, d]; k, v
+    bfloat16 [B, H, Nk, d]. MXFP8: q, k, v, do uint8 e4m3 bytes with
+    q_scale / k_scale / v_scale / do_scale uint8 [B, H, N/32, 4] (see
+    mx_quantize), o bfloat16. lse: float32 [B, H, Nq]. dQ, dK, dV are
+    bfloat16. The float32 workspace (8*B*H*Nq bytes) is allocated here unless
+    given."""
     import torch
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor [B, H, N, d]")
+    mx = q.dtype == torch.uint8
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.dtype != (torch.uint8 if mx else torch.bfloat16):
+            raise ValueError(f"{name} must be a contiguous {'uint8' if mx else 'bfloat16'} GPU tensor [B, H, N, d]")
+    if not o.is_cuda or not o.is_contiguous() or o.dtype != torch.bfloat16:
+        raise ValueError("o must be a contiguous bfloat16 GPU tensor [B, H, Nq, d]")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     if k.shape != (B, H, Nk, d) or v.shape != k.shape or o.shape != q.shape or do.shape != q.shape:
         raise ValueError("shape mismatch")
     if not lse.is_cuda or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, Nq]")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    sptr = [0, 0, 0, 0]
+    if mx:
+        for i, (name, t, n) in enumerate((("q_scale", q_scale, Nq), ("k_scale", k_scale, Nk), ("v_scale", v_scale, Nk),
+                                          ("do_scale", do_scale, Nq))):
+            if t is None or t.dtype != torch.uint8 or not t.is_contiguous() or tuple(t.shape) != (B, H, n // 32, d // 32):
+                raise ValueError(f"{name} must be contiguous uint8 [B, H, N/32, d/32]")
+            sptr[i] = t.data_ptr()
+    dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.bfloat16, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.bfloat16, device=q.device) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t.shape != ref.shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"{name} has the wrong shape, dtype or layout")
@@ -274,11 +292,31 @@ def bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None
     if workspace is None:
         workspace = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                        workspace.numel() * workspace.element_size(), B, H, Nq, Nk, d, _causal(causal), scale,
-                        ATTN_BF16, _stream_ptr(stream, q.device)))
+    _check(lib.attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), B, H, Nq, Nk, d, _causal(causal), scale,
+                           ATTN_MXFP8_E4M3 if mx else ATTN_BF16, sptr[0], sptr[1], sptr[2], sptr[3],
+                           _stream_ptr(stream, q.device)))
     return dq, dk, dv
+
+
+def mx_quantize(x, out=None, scale=None, stream=None):
+    """bf16 [..., N, 128] (N a multiple of 32) to e4m3 bytes of the same shape
+    and one E8M0 byte per 32x32 block [..., N/32, 4] (attn_mx_quantize)."""
+    import torch
+    lib = load_library()
+    if not x.is_cuda or x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() < 2:
+        raise ValueError("x must be a contiguous bfloat16 GPU tensor [..., N, d]")
+    *lead, n, d = x.shape
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    scale = torch.empty((*lead, n // 32, d // 32), dtype=torch.uint8, device=x.device) if scale is None else scale
+    if out.shape != x.shape or out.dtype != torch.uint8 or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    if tuple(scale.shape) != (*lead, n // 32, d // 32) or scale.dtype != torch.uint8 or not scale.is_contiguous():
+        raise ValueError("scale has the wrong shape, dtype or layout")
+    _check(lib.attn_mx_quantize(x.data_ptr(), out.data_ptr(), scale.data_ptr(), x.numel() // d, d,
+                                _stream_ptr(stream, x.device)))
+    return out, scale
 
 
 def mx_scale_offsets(cu_seqlens, total: int, align: int = 32, out=None, stream=None):

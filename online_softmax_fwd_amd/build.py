@@ -30,6 +30,7 @@ SOURCES = [
     "attn_fwd_mxfp8.hip",
     "attn_mx_layout.hip",
     "attn_bwd_bf16.hip",
+    "attn_bwd_mxfp8.hip",
 ]
 
 COMMON_FLAGS = [

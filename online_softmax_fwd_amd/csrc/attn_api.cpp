@@ -332,34 +332,45 @@ long long attn_bwd_workspace_bytes(int B, int H, int Nq) {
   return 8LL * B * H * Nq;
 }
 
-int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
-             void* dK, void* dV, float* workspace, long long workspace_bytes, int B, int H, int Nq, int Nk, int d,
-             int causal, float scale, int dtype, void* stream) {
-  if (dtype != ATTN_BF16) return fail(ATTN_E_DTYPE, "attn_bwd takes ATTN_BF16 (got dtype %d)", dtype);
+int attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
+                void* dK, void* dV, float* workspace, long long workspace_bytes, int B, int H, int Nq, int Nk, int d,
+                int causal, float scale, int dtype, const uint8_t* q_scale, const uint8_t* k_scale,
+                const uint8_t* v_scale, const uint8_t* do_scale, void* stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_MXFP8_E4M3)
+    return fail(ATTN_E_DTYPE, "the backward pass takes ATTN_BF16 or ATTN_MXFP8_E4M3 (got dtype %d)", dtype);
+  const bool mx = dtype == ATTN_MXFP8_E4M3;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
     return fail(ATTN_E_SHAPE, "negative size (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
-  if (d != 64 && d != 128) return fail(ATTN_E_HEADDIM, "attn_bwd supports d=64 and d=128 (got %d)", d);
+  if (mx ? d != 128 : (d != 64 && d != 128))
+    return fail(ATTN_E_HEADDIM, "the backward pass supports d=64 and d=128 for bf16, d=128 for MXFP8 (got %d)", d);
   if (causal < 0 || causal > 2) return fail(ATTN_E_SHAPE, "causal=%d is not 0, 1 or 2", causal);
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(ATTN_E_SCALE, "scale=%g must be finite and > 0", scale);
   if ((long long)B * H == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
   const long long n_t = (std::max(Nq, Nk) + 127) / 128;
   if ((long long)B * H * n_t > 0x7FFFFFFFLL || Nq > (1 << 30) || Nk > (1 << 30))
     return fail(ATTN_E_SHAPE, "sizes too large (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
+  if (mx && (Nq % 32 != 0 || Nk % 32 != 0))
+    return fail(ATTN_E_SHAPE, "MXFP8 needs Nq and Nk to be multiples of 32 (Nq=%d Nk=%d)", Nq, Nk);
   // one (batch, head) slice of Q, K, V or dO is addressed with 32-bit byte
   // offsets, up to one tile past the end
-  if (((long long)std::max(Nq, Nk) + 256) * d * 2 > 0x7FFFFFFFLL)
+  if (((long long)std::max(Nq, Nk) + 256) * d * (mx ? 1 : 2) > 0x7FFFFFFFLL)
     return fail(ATTN_E_SHAPE, "one (batch, head) slice must stay under 2 GiB (Nq=%d Nk=%d d=%d)", Nq, Nk, d);
   if (workspace_bytes < attn_bwd_workspace_bytes(B, H, Nq))
     return fail(ATTN_E_SHAPE, "workspace of %lld bytes; attn_bwd_workspace_bytes gives %lld", workspace_bytes,
                 attn_bwd_workspace_bytes(B, H, Nq));
-  // tensors with no elements (Nq = 0: Q, O, dO, LSE, dQ, workspace; Nk = 0:
-  // K, V, dK, dV) are never touched and may be NULL
-  if (Nq > 0 && (!Q || !O || !dO || !LSE || !dQ || !workspace))
-    return fail(ATTN_E_NULLPTR, "Q, O, dO, LSE, dQ and workspace must be non-NULL");
-  if (Nk > 0 && (!K || !V || !dK || !dV)) return fail(ATTN_E_NULLPTR, "K, V, dK and dV must be non-NULL");
+  // tensors with no elements (Nq = 0: Q, O, dO, LSE, dQ, workspace and the Q /
+  // dO scales; Nk = 0: K, V, dK, dV and their scales) are never touched and
+  // may be NULL
+  if (Nq > 0 && (!Q || !O || !dO || !LSE || !dQ || !workspace || (mx && (!q_scale || !do_scale))))
+    return fail(ATTN_E_NULLPTR, "Q, O, dO, LSE, dQ, workspace (and for MXFP8 q_scale, do_scale) must be non-NULL");
+  if (Nk > 0 && (!K || !V || !dK || !dV || (mx && (!k_scale || !v_scale))))
+    return fail(ATTN_E_NULLPTR, "K, V, dK, dV (and for MXFP8 k_scale, v_scale) must be non-NULL");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(LSE) ||
       !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
     return fail(ATTN_E_ALIGN, "every tensor and the workspace must be 16-byte aligned");
+  if (mx && ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+              reinterpret_cast<uintptr_t>(v_scale) | reinterpret_cast<uintptr_t>(do_scale)) & 3u))
+    return fail(ATTN_E_ALIGN, "MX scale pointers must be 4-byte aligned");
   attn::BwdArgs a;
   a.q = Q;
   a.k = K;
@@ -371,6 +382,10 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   a.d_k = dK;
   a.d_v = dV;
   a.ws = workspace;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.do_scale = do_scale;
   a.B = B;
   a.H = H;
   a.Nq = Nq;
@@ -380,7 +395,29 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   a.bottom_right = causal == 2;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
-  hipError_t e = attn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = mx ? attn::launch_bwd_mxfp8(a, st) : attn::launch_bwd_bf16(a, st);
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
+             void* dK, void* dV, float* workspace, long long workspace_bytes, int B, int H, int Nq, int Nk, int d,
+             int causal, float scale, int dtype, void* stream) {
+  if (dtype != ATTN_BF16)
+    return fail(ATTN_E_DTYPE, "attn_bwd takes ATTN_BF16 (got dtype %d); MXFP8 needs its scales: attn_bwd_ex", dtype);
+  return attn_bwd_ex(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H, Nq, Nk, d, causal, scale,
+                     dtype, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+int attn_mx_quantize(const void* x, uint8_t* q, uint8_t* scale, long long rows, int d, void* stream) {
+  if (d != 128) return fail(ATTN_E_HEADDIM, "attn_mx_quantize supports d=128 (got %d)", d);
+  if (rows < 0 || rows % 32 != 0 || rows / 32 > 0x7FFFFFFFLL)
+    return fail(ATTN_E_SHAPE, "rows=%lld must be a non-negative multiple of 32 (blocks are 32x32)", rows);
+  if (rows == 0) return ATTN_OK;
+  if (!x || !q || !scale) return fail(ATTN_E_NULLPTR, "x, q and scale must be non-NULL");
+  if (!aligned16(x) || !aligned16(q)) return fail(ATTN_E_ALIGN, "x and q must be 16-byte aligned");
+  hipError_t e = attn::launch_mx_quantize(x, q, scale, rows, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
 }

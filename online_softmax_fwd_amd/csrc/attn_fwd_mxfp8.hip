@@ -37,12 +37,10 @@
 // Epilogue: O / l (deferred normalisation) and LSE = ln2 * (m*c + log2 l).
 #include "attn_device.h"
 #include "attn_internal.h"
+#include "attn_mx_common.h"
 
 namespace attn {
 namespace {
-
-typedef int intx2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) intx2 lds_intx2;
 
 constexpr int kD = 128;
 constexpr int kRB = kD;                        // bytes per K/V row (one byte per element)
@@ -55,63 +53,12 @@ constexpr int kTile = kBN * kRB;               // bytes per K or V tile
 constexpr int kLoads = kBN * kCH / 64 / kWaves;  // wave-loads per wave per tensor per tile
 static_assert(kLoads * 64 * kWaves == kBN * kCH, "tile split");
 
-// S^T A-operand row m reads key key_of_row(m) of its 32-key block: the 32x32
-// output then holds keys 16h + e (e = 0..15) in lane half h.
-__device__ __forceinline__ int key_of_row(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
-
 // Swizzles of the 16-byte chunks (position c ^ f(r)). The K reads of one
 // instruction take one chunk from 16 rows (the permuted key rows above) per
 // 16-lane group; the V transpose reads take 2 chunks from 16 rows. Rows are
 // 128 bytes, so a 256-byte bank line holds two rows.
 __device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ ((r >> 4) << 2)) & 7; }
 __device__ __forceinline__ int swz_v(int r) { return ((r >> 1) & 3) << 1; }
-
-__device__ __forceinline__ void wait_own_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-
-__device__ __forceinline__ float pl_max_halves(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
-}
-__device__ __forceinline__ float pl_sum_halves(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
-}
-
-__device__ __forceinline__ float max16(const floatx16& x) {
-  float t[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = __builtin_fmaxf(x[e], x[e + 8]);
-#pragma unroll
-  for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-    for (int e = 0; e < w; ++e) t[e] = __builtin_fmaxf(t[e], t[e + w]);
-  return t[0];
-}
-__device__ __forceinline__ float sum16(const floatx16& x) {
-  float t[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = x[e] + x[e + 8];
-#pragma unroll
-  for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-    for (int e = 0; e < w; ++e) t[e] = t[e] + t[e + w];
-  return t[0];
-}
-
-// E8M0 byte of the smallest power of two X with amax / X <= 448 (e4m3's
-// largest finite value), read off the float32 bits of amax >= 0: with
-// amax = 1.f * 2^e, X = 2^(e-8) when 1.f <= 1.75, else 2^(e-7). Zero gives
-// X = 1. Clamped to [1, 253] so X and 1/X are normal floats.
-__device__ __forceinline__ uint32_t e8m0_of(float amax) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, amax);
-  const int eb = (int)((u >> 23) & 0xFF);
-  int byte = eb - 8 + ((u & 0x7FFFFF) > 0x600000 ? 1 : 0);
-  byte = eb == 0 ? 127 : byte;
-  return (uint32_t)__builtin_amdgcn_fmed3f((float)byte, 1.0f, 253.0f);
-}
 
 // P quantisation: kPBlock = one E8M0 scale per 32-key block from the block
 // amax (the MXFP8 page's design); kPFixedE4M3 / kPFixedE5M2 = P times the
@@ -168,7 +115,7 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   const uint32_t tile_bytes = (uint32_t)kBN * rs;
 
   // ---- per-lane constants --------------------------------------------------
-  const int krow = key_of_row(l32);
+  const int krow = mx_key_of_row(l32);
   uint32_t koff[2][2];  // [d step s][which 16-byte half]
 #pragma unroll
   for (int s = 0; s < 2; ++s)

@@ -42,6 +42,10 @@ struct BwdArgs {
   void* d_k;
   void* d_v;
   float* ws;                // 2 floats per query row: LSE * log2(e), D = rowsum(dO * O)
+  const uint8_t* q_scale;   // MXFP8: E8M0 per 32x32 block of Q, K, V, dO
+  const uint8_t* k_scale;
+  const uint8_t* v_scale;
+  const uint8_t* do_scale;
   int B, H, Nq, Nk, d;
   int causal;               // 0 or 1
   int bottom_right;
@@ -54,6 +58,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 // prep pass, dK/dV kernel, dQ kernel, in that order on `stream`
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_mxfp8(const BwdArgs& a, hipStream_t stream);
+// bf16 [rows, 128] -> e4m3 + one E8M0 byte per 32x32 block; rows % 32 == 0
+hipError_t launch_mx_quantize(const void* x, uint8_t* q, uint8_t* scale, long long rows, hipStream_t stream);
 // p_mode: 0 = P scaled per 32-key block, 1 = fixed 2^8 scale with E4M3 P,
 // 2 = fixed 2^8 scale with E5M2 P
 hipError_t launch_fwd_mxfp8(const FwdArgs& a, int p_mode, hipStream_t stream);

@@ -28,7 +28,8 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert names == sorted(["attn_bwd", "attn_bwd_workspace_bytes", "attn_exp2", "attn_fwd", "attn_fwd_ex",
+    assert names == sorted(["attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes", "attn_exp2", "attn_fwd",
+                            "attn_fwd_ex", "attn_mx_quantize",
                             "attn_fwd_stats", "attn_fwd_varlen",
                             "attn_fwd_varlen_ex", "attn_last_error", "attn_mix_sixteenths",
                             "attn_mx_scale_offsets", "attn_mx_scale_scatter"])
@@ -278,3 +279,46 @@ def test_bwd_validation_errors(lib, kw, code):
 def test_bwd_nothing_to_do(lib, kw):
     assert _bwd(lib, Q=None, K=None, V=None, O=None, dO=None, LSE=None, dQ=None, dK=None, dV=None, ws=None,
                 wsb=0, **kw) == 0
+
+
+def _bwd_ex(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, LSE=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE, ws=FAKE, wsb=1 << 20,
+             B=2, H=3, Nq=96, Nk=128, d=128, causal=0, scale=0.088, dtype=2, qs=FAKE, ks=FAKE, vs=FAKE, ds=FAKE)
+    a.update(kw)
+    return lib.attn_bwd_ex(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"], a["dK"], a["dV"], a["ws"],
+                           a["wsb"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"],
+                           a["qs"], a["ks"], a["vs"], a["ds"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), -4),                  # the backward pass takes the per-block MXFP8 code
+    (dict(dtype=0), -4),
+    (dict(d=64), -3),                     # MXFP8 is d = 128 only
+    (dict(Nq=100), -2), (dict(Nk=40), -2),  # multiples of 32
+    (dict(qs=None), -1), (dict(ds=None), -1), (dict(vs=None), -1),
+    (dict(ks=FAKE + 2), -8), (dict(ds=FAKE + 1), -8),
+    (dict(wsb=8 * 2 * 3 * 96 - 8), -2),
+    (dict(dtype=1, d=192), -3),           # bf16 keeps its own checks
+])
+def test_bwd_ex_validation_errors(lib, kw, code):
+    assert _bwd_ex(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+def test_bwd_ex_bf16_ignores_scales(lib):
+    assert _bwd_ex(lib, dtype=1, qs=None, ks=None, vs=None, ds=None, B=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), -3), (dict(rows=33), -2), (dict(rows=-32), -2), (dict(x=None), -1), (dict(sc=None), -1),
+    (dict(x=FAKE + 2), -8), (dict(q=FAKE + 8), -8),
+])
+def test_mx_quantize_validation(lib, kw, code):
+    a = dict(x=FAKE, q=FAKE, sc=FAKE, rows=64, d=128)
+    a.update(kw)
+    assert lib.attn_mx_quantize(a["x"], a["q"], a["sc"], a["rows"], a["d"], None) == code
+    assert lib.attn_last_error()
+
+
+def test_mx_quantize_nothing_to_do(lib):
+    assert lib.attn_mx_quantize(None, None, None, 0, 128, None) == 0
