@@ -19,7 +19,7 @@ Prints ONE JSON line. Besides the contract fields it carries
                 (null when no counter run covers these kernel sources)
   rescale       lagging-max rescale counts per mode, from one counting launch
                 (attn_fwd_stats) outside the timed region
-  backward      bf16 workloads at d 64 and 128: the backward pass (attn_bwd) on the same
+  backward      bf16 workloads at d 64 and 128 and the MXFP8 workload: the backward pass (attn_bwd) on the same
                 inputs with the forward's O and LSE and a seeded dO, timed
                 after the forward's timed region (HIP events per call on the
                 launch stream); FLOPs counted as 2.5 x the forward's (the five
@@ -140,20 +140,24 @@ def fwd_kernel_name(w, causal: bool) -> str:
     return f"fwd_{w.dtype}_kernel"
 
 
-def bench_backward(attn, w, q, k, v, outs, stream, args):
+def bench_backward(attn, w, q, k, v, outs, stream, args, scales=None):
     import numpy as np
     import torch
     from attn_inputs import make_grad_output
     bits, _ = make_grad_output((w.B, w.H, w.Nq, w.d), w.seed + 1)
     do = torch.from_numpy(bits.view(np.int16)).to(q.device).view(torch.bfloat16)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    extra = {}
+    if w.dtype == "mxfp8":  # dO in square 32x32 blocks, quantised once outside the timed calls
+        do, dos = attn.mx_quantize(do, stream=stream)
+        extra = dict(scales, do_scale=dos)
+    dq, dk, dv = (torch.empty(t.shape, dtype=torch.bfloat16, device=q.device) for t in (q, k, v))
     ws = torch.empty(2 * w.B * w.H * w.Nq, dtype=torch.float32, device=q.device)
     res = {}
     for c in w.causal:
         o, lse = outs[c]
 
         def call():
-            attn.bwd(q, k, v, o, do, lse, causal=c, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+            attn.bwd(q, k, v, o, do, lse, causal=c, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream, **extra)
         for _ in range(args.bwd_warmup):
             call()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -169,7 +173,8 @@ def bench_backward(attn, w, q, k, v, outs, stream, args):
         res["causal" if c else "noncausal"] = {
             "ms_mean": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
             "pct_of_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[w.dtype], 2)}
-    res["flops_note"] = "2.5 x the forward's FLOPs per call; kernels: bwd_prep, bwd_dkdv, bwd_dq"
+    res["flops_note"] = ("2.5 x the forward's FLOPs per call; kernels: prep, dK/dV, dQ" +
+                         ("; dO quantised once outside the timed calls" if w.dtype == "mxfp8" else ""))
     return res
 
 
@@ -311,8 +316,8 @@ def main():
             "row_tile_steps": st[0], "row_rescales": st[1], "wave_tile_steps": st[2], "wave_rescales": st[3],
             "row_frac": round(st[1] / max(st[0], 1), 6), "wave_frac": round(st[3] / max(st[2], 1), 6)}
     result["rescale"] = rescale
-    if w.dtype == "bf16" and w.d in (64, 128) and not args.no_bwd:    # the backward pass's head dims
-        result["backward"] = bench_backward(attn, w, q, k, v, outs, stream, args)
+    if not args.no_bwd and ((w.dtype == "bf16" and w.d in (64, 128)) or (w.dtype == "mxfp8" and args.fp8_p == "block")):
+        result["backward"] = bench_backward(attn, w, q, k, v, outs, stream, args, scales)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, w.causal)
     print(json.dumps(result), flush=True)

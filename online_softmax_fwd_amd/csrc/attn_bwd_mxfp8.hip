@@ -15,9 +15,10 @@
 //
 //   bwd_mx_prep_kernel   D_i = sum_c dO_ic O_ic (dO dequantised, O bf16) and
 //                        LSE_i * log2(e) (+inf for rows without keys).
-//   bwd_mx_dkdv_kernel   4 waves x 32 keys; K and V rows in registers as B
-//                        operands; 64-query tiles of Q and dO (e4m3) DMA'd to
-//                        LDS. Per tile and 32-query half: S = Q K^T and
+//   bwd_mx_dkdv_kernel   4 waves x 32 keys; the workgroup's K and V rows in
+//                        LDS as B operands (in registers they spill next to
+//                        the dK and dV accumulators: 30 % slower); 64-query
+//                        tiles of Q and dO (e4m3) DMA'd to LDS. Per tile and 32-query half: S = Q K^T and
 //                        dP = dO V^T (permuted rows, so each lane holds 16
 //                        consecutive queries), P = 2^(S*c - LSE*log2 e),
 //                        dS = P * (dP - D). P <= 1 exactly (the true LSE is
@@ -236,6 +237,8 @@ void bwd_mx_dkdv_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict
   __shared__ __attribute__((aligned(1024))) char d1s[kTile];
   __shared__ __attribute__((aligned(16))) float w0s[2 * kTileRows];
   __shared__ __attribute__((aligned(16))) float w1s[2 * kTileRows];
+  __shared__ __attribute__((aligned(1024))) char kls[32 * kNW * kRB];  // the workgroup's K rows
+  __shared__ __attribute__((aligned(1024))) char vls[32 * kNW * kRB];  // and V rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -267,9 +270,30 @@ void bwd_mx_dkdv_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict
   const u32x4 rdo = raw_buffer_rsrc(dO + qbase, (uint32_t)(Nq * kRB));
   const u32x4 rw = raw_buffer_rsrc(ws + (size_t)bh * Nq * 2, (uint32_t)(Nq * 8));
 
-  i32x8 kf[2], vf[2];
-  load_row_mx(kf, K + kbase + (size_t)(key_ok ? key : 0) * kD, key_ok, hh);
-  load_row_mx(vf, V + kbase + (size_t)(key_ok ? key : 0) * kD, key_ok, hh);
+  // K and V rows of the workgroup's keys stay in LDS (registers would spill
+  // next to the dK and dV accumulators); chunk c of row r sits at c ^ f(r),
+  // f(r) = (r >> 1) & 7, so the B-operand reads (16 rows, one chunk) hit 16
+  // bank groups. Keys past Nk read as zero.
+  {
+    const u32x4 rk = raw_buffer_rsrc(K + kbase, (uint32_t)(Nk * kRB));
+    const u32x4 rv = raw_buffer_rsrc(V + kbase, (uint32_t)(Nk * kRB));
+#pragma unroll
+    for (int i = 0; i < 32 * kNW * kCH / 64 / kNW; ++i) {
+      const int pos = 64 * (wave + kNW * i) + lane;
+      const int r = pos / kCH, p = pos % kCH;
+      const uint32_t off = (uint32_t)(k0 + r) * kRB + 16 * (p ^ ((r >> 1) & 7));
+      dma16(rk, kls + 1024 * (wave + kNW * i), off);
+      dma16(rv, vls + 1024 * (wave + kNW * i), off);
+    }
+  }
+  const int krow = 32 * wave + l32;
+  auto kv_operand = [&](const char* base, int s) __attribute__((always_inline)) -> i32x8 {
+    const char* p = base + krow * kRB;
+    const int f = (l32 >> 1) & 7;
+    const u32x4 lo = *(const u32x4*)(p + 16 * ((4 * s + hh) ^ f));
+    const u32x4 hi = *(const u32x4*)(p + 16 * ((4 * s + 2 + hh) ^ f));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
   const int kb_idx = kw0 / 32;
   const int ksc = (int)(scale_word(KS + (size_t)bh * nkb * 4, kb_idx, nkb) >> (8 * hh));
   const int vsc = (int)(scale_word(VS + (size_t)bh * nkb * 4, kb_idx, nkb) >> (8 * hh));
@@ -303,10 +327,14 @@ void bwd_mx_dkdv_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict
       const int qsc = (int)(scale_word(qsb, qb, nqb) >> (8 * hh));
       const int gsc = (int)(scale_word(dsb, qb, nqb) >> (8 * hh));
       floatx16 s = {}, dp = {};
-      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row_operand(qs, to, sb, 0), kf[0], s, 0, 0, 0, qsc, 0, ksc);
-      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row_operand(qs, to, sb, 1), kf[1], s, 0, 0, 2, qsc, 2, ksc);
-      dp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row_operand(dos, to, sb, 0), vf[0], dp, 0, 0, 0, gsc, 0, vsc);
-      dp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row_operand(dos, to, sb, 1), vf[1], dp, 0, 0, 2, gsc, 2, vsc);
+      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row_operand(qs, to, sb, 0), kv_operand(kls, 0), s, 0, 0, 0,
+                                                          qsc, 0, ksc);
+      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row_operand(qs, to, sb, 1), kv_operand(kls, 1), s, 0, 0, 2,
+                                                          qsc, 2, ksc);
+      dp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row_operand(dos, to, sb, 0), kv_operand(vls, 0), dp, 0, 0,
+                                                           0, gsc, 0, vsc);
+      dp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row_operand(dos, to, sb, 1), kv_operand(vls, 1), dp, 0, 0,
+                                                           2, gsc, 2, vsc);
       // element e of lane half h holds query q0 + 32 sb + 16 h + e
       const int qe0 = q0 + 32 * sb + 16 * hh;
       const float4* wp = (const float4*)(wsd + 2 * (32 * sb + 16 * hh));
