@@ -55,11 +55,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kUnitScales = 0x7F7F7F7Fu;  // four E8M0 bytes of scale 1
 
 // Chunk swizzle of tiles read both as permuted rows and through the
-// transpose read (position c ^ f(r)): bits 2 and 4 of the row, chosen by
-// exhaustive search so that both read patterns touch every one of the 64
-// banks the minimum number of times. It ignores row bits 3 and 5, the steps
-// between the rows of one transpose read and between 32-row blocks.
-__device__ __forceinline__ int swz_mx(int r) { return ((r >> 1) & 2) | ((r >> 2) & 4); }
+// transpose read (position c ^ f(r)). LDS serves a 16-byte read 16 lanes at a
+// time and an 8-byte read 32 lanes at a time, and each such group must touch
+// 64 different banks; f, a map of row bits 1, 2 and 4 found by exhaustive
+// search over such maps, does that for both patterns. It ignores row bits 3
+// and 5, the steps between the rows of one transpose read and between 32-row
+// blocks, so one per-lane offset serves all of them.
+__device__ __forceinline__ int swz_mx(int r) { return (r & 6) ^ ((r >> 4) & 1); }
 
 struct MxOffsets {
   uint32_t row[2][2];     // permuted-row read: [64-wide d step][16-byte half]
