@@ -58,10 +58,9 @@ static_assert(kLoads * 64 * kWaves == kBN * kCH, "tile split");
 // lanes at a time, and each group must touch 64 different banks: the K reads
 // (one chunk of 16 permuted key rows per 16 lanes) and the V transpose reads
 // (rows 16h + 0..7 and +8, +32, +40; 2 chunks) both do with f below, a map of
-// row bits 1, 2 and 4 (rows are 128 bytes, two per bank line). Measured: 0
-// bank-conflict cycles against 0.33 per LDS-active cycle with the previous
-// per-tensor swizzles, which kept whole 64-lane instructions balanced but not
-// each group (+1-2 %).
+// row bits 1, 2 and 4 (rows are 128 bytes, two per bank line). Measured
+// (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE): 0, against 0.33 with the
+// previous per-tensor swizzles, and 1-2 % faster.
 __device__ __forceinline__ int swz_k(int r) { return (r & 6) ^ ((r >> 4) & 1); }
 __device__ __forceinline__ int swz_v(int r) { return (r & 6) ^ ((r >> 4) & 1); }
 
