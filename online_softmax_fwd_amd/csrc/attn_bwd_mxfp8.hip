@@ -123,13 +123,26 @@ __device__ __forceinline__ uint32_t scale_word(const uint8_t* base, int blk, int
   return blk < nblk ? *(const uint32_t*)(base + (size_t)blk * 4) : kUnitScales;
 }
 
-// Largest |x| over the wave's 64 lanes x 16 elements (one 32x32 block).
+// Largest |x| over the wave's 64 lanes x 16 elements (one 32x32 block): a
+// v_maximum3_f32 tree in the lane (|x| as a source modifier), then DPP lane
+// swaps within each row of 16 (xor 1, xor 2, the other half of 8, the other
+// half of 16) and the row and wave-half swaps of v_permlane16/32_swap.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_absmax(const floatx16& x) {
-  float m = 0.0f;
+  float t[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(x[e]));
-#pragma unroll
-  for (int w = 1; w < 32; w <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, w));
+  for (int e = 0; e < 16; ++e) t[e] = __builtin_fabsf(x[e]);
+  float m = MaxTree3<16>::run(t);
+  m = vmax(m, dpp_mov<0xB1>(m));   // quad_perm [1,0,3,2]
+  m = vmax(m, dpp_mov<0x4E>(m));   // quad_perm [2,3,0,1]
+  m = vmax(m, dpp_mov<0x141>(m));  // row_half_mirror
+  m = vmax(m, dpp_mov<0x140>(m));  // row_mirror
+  const uint32_t u = __builtin_bit_cast(uint32_t, m);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  m = vmax(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
   return pl_max_halves(m);
 }
 

@@ -81,14 +81,8 @@ __device__ __forceinline__ int swz_k(int r) { return (D == 128 || D == 256) ? (r
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return (D == 128 || D == 256) ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-
-
-
-
-
-
-// Sum and max of a wave's 32 per-lane scores as balanced trees (depth 5 and
-// 4) instead of serial chains, so the softmax stage is not latency-bound.
+// Sum of a lane's scores as a balanced tree instead of a serial chain, so the
+// softmax stage is not latency-bound (the max tree is tree_max).
 template <int KB>
 __device__ __forceinline__ float tree_sum(const floatx16 (&x)[KB]) {
   float t[8 * KB];
@@ -100,19 +94,6 @@ __device__ __forceinline__ float tree_sum(const floatx16 (&x)[KB]) {
   for (int w = 4 * KB; w >= 1; w >>= 1)
 #pragma unroll
     for (int e = 0; e < w; ++e) t[e] = t[e] + t[e + w];
-  return t[0];
-}
-template <int KB>
-__device__ __forceinline__ float tree_max(const floatx16 (&x)[KB]) {
-  float t[8 * KB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[8 * kb + e] = __builtin_fmaxf(x[kb][e], x[kb][e + 8]);
-#pragma unroll
-  for (int w = 4 * KB; w >= 1; w >>= 1)
-#pragma unroll
-    for (int e = 0; e < w; ++e) t[e] = __builtin_fmaxf(t[e], t[e + w]);
   return t[0];
 }
 
@@ -330,7 +311,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     const float mx = pl_max_halves(tree_max<KB>(s));
 
-    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float m_new = vmax(m_run, mx);
     const float acc = (m_run - m_new) * c;  // -inf on a row's first block
     const bool seen = mx > kNegInf;
     const bool commit = seen && !(acc >= -tau);
@@ -575,7 +556,7 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
         }
     }
     const float mx = pl_max_halves(tree_max<KB>(s));
-    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float m_new = vmax(m_run, mx);
     const float acc = (m_run - m_new) * c;
     const bool seen = mx > kNegInf;
     const bool commit = seen && !(acc >= -tau);

@@ -228,8 +228,8 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
     // block maxima (reused for the P scales) and the row max
     const float bm0 = pl_max_halves(max16(s[0]));
     const float bm1 = pl_max_halves(max16(s[1]));
-    const float mx = __builtin_fmaxf(bm0, bm1);
-    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float mx = vmax(bm0, bm1);
+    const float m_new = vmax(m_run, mx);
     const float acc = (m_run - m_new) * c;
     const bool seen = mx > kNegInf;
     const bool commit = seen && !(acc >= -tau);

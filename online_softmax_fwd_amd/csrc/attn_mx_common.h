@@ -16,14 +16,10 @@ typedef __attribute__((address_space(3))) intx2 lds_intx2;
 __device__ __forceinline__ int mx_key_of_row(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
 
 __device__ __forceinline__ float max16(const floatx16& x) {
-  float t[8];
+  float t[16];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = __builtin_fmaxf(x[e], x[e + 8]);
-#pragma unroll
-  for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-    for (int e = 0; e < w; ++e) t[e] = __builtin_fmaxf(t[e], t[e + w]);
-  return t[0];
+  for (int e = 0; e < 16; ++e) t[e] = x[e];
+  return MaxTree3<16>::run(t);
 }
 __device__ __forceinline__ float sum16(const floatx16& x) {
   float t[8];
