@@ -24,11 +24,11 @@
 //   P -> e4m3          per 32-key block, as the MXFP8 page's "Softmax conversion
 //                      and unroll-KV" section describes: the block amax comes
 //                      from the softmax block max already computed (exp is
-//                      monotone: amax = 2^((blockmax - m) * c), one exp per 32
-//                      keys), the E8M0 byte from the float32 exponent and
-//                      mantissa bits of amax (smallest power of two X with
-//                      amax / X <= 448), then P / X is converted with
-//                      v_cvt_pk_fp8_f32.
+//                      monotone: amax = 2^a, a = (blockmax - m) * c), the
+//                      E8M0 exponent of the smallest power of two X with
+//                      amax / X <= 448 as ceil(a - log2 448) (the same rule,
+//                      taken in the log domain: no exponential and no bit
+//                      decoding), then P / X is converted with v_cvt_pk_fp8_f32.
 //   O^T += V^T P^T     4 MFMAs (d blocks), A = V^T via ds_read_b64_tr_b8, B = P
 //                      bytes straight from the S^T registers: the K rows
 //                      feeding S^T are permuted so lane half h holds keys
@@ -72,6 +72,17 @@ __device__ __forceinline__ int swz_v(int r) { return (r & 6) ^ ((r >> 4) & 1); }
 // max_offset + tau < log2(largest finite value), so the cast never saturates.
 enum { kPBlock = 0, kPFixedE4M3 = 1, kPFixedE5M2 = 2 };
 constexpr int kMaxOffset = 8;
+
+// Exponent k of the P scale X = 2^k of a 32-key block from its largest score
+// bm: amax = 2^a with a = bm*c - mc, and the smallest power of two with
+// amax / X <= 448 has k = ceil(a - log2 448) (the E8M0 rule, taken in the log
+// domain, where the softmax already is: no exponential or bit decoding of
+// amax). Clamped to [-126, 127] so that X is a normal float and its byte a
+// finite E8M0; a fully masked block (a = -inf) takes -126.
+__device__ __forceinline__ float p_scale_exponent(float bm, float c, float mc) {
+  constexpr float kLog2Max = 8.80735492205760410f;  // log2(448)
+  return __builtin_amdgcn_fmed3f(__builtin_ceilf(__builtin_fmaf(bm, c, -(mc + kLog2Max))), -126.0f, 127.0f);
+}
 
 // PACKED: a batch of sequences packed token-major ([total, H, d] data,
 // [scale rows, H, d/32] scales at per-sequence scale offsets); lengths need
@@ -250,18 +261,19 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
     }
     const float mc = (m_run > kNegInf) ? m_run * c : 0.0f;
 
-    // P -> e4m3 per 32-key block: the block amax from the reused block max
-    // (P is monotone in s), its E8M0 byte sb, and P / X with X = 2^(sb - 127)
-    // taken straight from the exponential, 2^(s*c - mc + 127 - sb), so the
-    // quantiser needs no multiply; l adds the block sums times X.
-    uint32_t sb0, sb1;
+    // P -> e4m3 per 32-key block: the scale X = 2^k from the reused block max
+    // (P is monotone in s), its E8M0 byte sb = k + 127, and P / X taken
+    // straight from the exponential, 2^(s*c - mc - k), so the quantiser needs
+    // no multiply; l adds the block sums times X.
+    float k0f, k1f;  // X = 2^k of each block
     if constexpr (PMODE == kPBlock) {
-      sb0 = e8m0_of(exp2_hw(__builtin_fmaf(bm0, c, -mc)));
-      sb1 = e8m0_of(exp2_hw(__builtin_fmaf(bm1, c, -mc)));
+      k0f = p_scale_exponent(bm0, c, mc);
+      k1f = p_scale_exponent(bm1, c, mc);
     } else {
-      sb0 = sb1 = 127 - kMaxOffset;  // P is stored times 2^max_offset
+      k0f = k1f = (float)-kMaxOffset;  // P is stored times 2^max_offset
     }
-    const float bias0 = mc - (float)(127 - (int)sb0), bias1 = mc - (float)(127 - (int)sb1);
+    const uint32_t sb0 = (uint32_t)((int)k0f + 127), sb1 = (uint32_t)((int)k1f + 127);
+    const float bias0 = mc + k0f, bias1 = mc + k1f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[0][e] = exp2_sel<EMU16>(__builtin_fmaf(s[0][e], c, -bias0), e);
 #pragma unroll
@@ -271,7 +283,7 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
     i32x8 pq;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      int lo = 0, hi = 0;
+      int lo = undef_dword(), hi = undef_dword();
       if constexpr (PMODE == kPFixedE5M2) {
         lo = __builtin_amdgcn_cvt_pk_bf8_f32(s[0][4 * w], s[0][4 * w + 1], lo, false);
         lo = __builtin_amdgcn_cvt_pk_bf8_f32(s[0][4 * w + 2], s[0][4 * w + 3], lo, true);

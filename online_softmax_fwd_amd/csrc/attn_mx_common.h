@@ -32,6 +32,15 @@ __device__ __forceinline__ float sum16(const floatx16& x) {
   return t[0];
 }
 
+// A dword with no defined value: the old operand of the first of the two
+// v_cvt_pk_fp8_f32 that write a dword's low and high halves (an empty asm
+// defines it, so no register is cleared first).
+__device__ __forceinline__ int undef_dword() {
+  int v;
+  asm volatile("" : "=v"(v));
+  return v;
+}
+
 // E8M0 byte of the smallest power of two X with amax / X <= 448 (e4m3's
 // largest finite value), read off the float32 bits of amax >= 0: with
 // amax = 1.f * 2^e, X = 2^(e-8) when 1.f <= 1.75, else 2^(e-7). Zero gives
