@@ -9,6 +9,7 @@ namespace {
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
 // A-operand row m of the S^T MFMA reads key key_of_row(m) of its 32-key
 // block. With the 32x32 output layout (lane half h, element j <-> row 8*(j/4)

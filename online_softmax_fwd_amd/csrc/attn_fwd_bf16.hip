@@ -97,6 +97,15 @@ __device__ __forceinline__ float tree_sum(const floatx16 (&x)[KB]) {
   return t[0];
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, in order
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The MFMA phase as one software-pipelined sequence: the PV MFMAs of the
 // previous tile, then the S^T MFMAs of the current tile. Operands come from
@@ -104,13 +113,12 @@ __device__ __forceinline__ float tree_sum(const floatx16 (&x)[KB]) {
 // durations long), and consecutive MFMAs rotate over independent accumulators
 // (the 4 (d=128) or 2 (d=64) blocks of O^T, then the 2 blocks of S^T).
 // While the first operands are in flight the wave converts the previous
-// tile's float32 P (left in s by the softmax stage) to bf16 and folds its row
-// sum into l, so that VALU work rides in the MFMA stage's idle issue slots.
+// tile's float32 P (left in s by the softmax stage) to bf16.
 // sched_barrier pins the issue order so the reads stay ahead.
 // ---------------------------------------------------------------------------
 template <int D, int KB, int RB, bool DO_PV, bool DO_QK>
-__device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&s)[KB], float& l_run, float alpha,
-                                              const bf16x8 (&qf)[D / 16], const char* ksrc, const char* vsrc,
+__device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&s)[KB], const bf16x8 (&qf)[D / 16],
+                                              uint32_t ksrc, uint32_t vsrc,
                                               const uint32_t (&koff)[D / 16], const uint32_t (&voff)[D / 32]) {
   constexpr int NDB = D / 32;
   constexpr int NPV = DO_PV ? NDB * KB * 2 : 0;
@@ -120,14 +128,14 @@ __device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&
   auto read = [&](int i) __attribute__((always_inline)) -> bf16x8 {
     if (i < NPV) {
       const int db = i % NDB, k = i / NDB, kb = k >> 1, cc = k & 1;
-      const char* vp = vsrc + voff[db] + (kb * 32 + 16 * cc) * RB;
-      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp));
-      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp + 4 * RB));
+      const uint32_t vp = voff[db] + vsrc + (kb * 32 + 16 * cc) * RB;
+      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(uintptr_t)(vp));
+      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(uintptr_t)(vp + 4 * RB));
       return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                                               __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
     }
     const int q = i - NPV, kb = q % KB, st = q / KB;
-    return *(const bf16x8*)(ksrc + kb * 32 * RB + koff[st]);
+    return *(const lds_bf16x8*)(uintptr_t)(koff[st] + ksrc + kb * 32 * RB);
   };
   bf16x8 ring[RING];
 #pragma unroll
@@ -141,7 +149,6 @@ __device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[kb][cc][e] = (__bf16)s[kb][8 * cc + e];
-    l_run = __builtin_fmaf(l_run, alpha, tree_sum<KB>(s));
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -163,6 +170,12 @@ __device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&
   }
 }
 
+// Depth of the ping-pong kernel's K/V ring in LDS (tiles of each): a tile's
+// DMA is issued 2S - 2 half-phases before its first reader. Depth 3 (96 KiB
+// of LDS) measured no faster than 2 at d = 128: the loads already arrive in
+// time.
+constexpr int kPingPongStages = 2;
+
 // ---------------------------------------------------------------------------
 // Ping-pong schedule. The 8 waves form two groups of 4 (one wave of each
 // group per SIMD). Each wave runs, per K/V tile j,
@@ -183,10 +196,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
   using C = Cfg<D, 64, 8>;
   constexpr int BN = C::BN, KB = C::KB;
-  __shared__ __attribute__((aligned(1024))) char kb0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char kb1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char vb0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char vb1[C::TILE];
+  constexpr int S = kPingPongStages;
+  __shared__ __attribute__((aligned(1024))) char kring[S * C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vring[S * C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -217,17 +229,24 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int diag = bottom_right ? Nk - Nq : 0;
 
   // ---- per-lane constants --------------------------------------------------
+  // LDS addresses of the K/V reads carry the ring's base in the register part
+  // (opaque to the compiler, so it does not split it off again), leaving
+  // slot + in-tile offsets below 64 KiB for the instruction's immediate field:
+  // the rings span more than a 16-bit offset reaches.
+  uint32_t kr = lds_address(kring), vbase = lds_address(vring);
+  asm volatile("" : "+s"(kr));
+  asm volatile("" : "+s"(vbase));
   uint32_t koff[D / 16], voff[D / 32], kld[C::LOADS], vld[C::LOADS];
   {
     const int krow = key_of_row(l32);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) koff[s] = krow * C::RB + 16 * ((2 * s + hh) ^ swz_k<D>(krow));
+    for (int s = 0; s < D / 16; ++s) koff[s] = kr + krow * C::RB + 16 * ((2 * s + hh) ^ swz_k<D>(krow));
     const int L = lane & 15, gidx = (lane >> 4) & 1;
     const int vr = 8 * hh + (L >> 2);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int cch = 4 * db + 2 * gidx + ((L & 3) >> 1);
-      voff[db] = vr * C::RB + 16 * (cch ^ swz_v<D>(vr)) + 8 * (L & 1);
+      voff[db] = vbase + vr * C::RB + 16 * (cch ^ swz_v<D>(vr)) + 8 * (L & 1);
     }
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
@@ -279,21 +298,33 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   float l_run = 0.0f;     // running denominator over this lane's half of the keys
   unsigned long long cnt[4] = {0, 0, 0, 0};
 
-  // DMA of this wave's share of K_{j+1} (into kdst) and V_j (into vdst)
-  auto load_tiles = [&](int j, char* kdst, char* vdst) __attribute__((always_inline)) {
+  // DMA batch b: this wave's share of K_{b+S-1} (into kdst) and V_{b+S-2}
+  // (into vdst), the tiles that MFMA phase b+S-1 reads
+  auto load_tiles = [&](int b, char* kdst, char* vdst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int slot = 1024 * (wave + 8 * i);
-      if (j + 1 < T)
-        dma16(rk, kdst + slot, kld[i] + (uint32_t)(j + 1) * tile_bytes);
-      if (j < T)
-        dma16(rv, vdst + slot, vld[i] + (uint32_t)j * tile_bytes);
+      if (b + S - 1 < T)
+        dma16(rk, kdst + slot, kld[i] + (uint32_t)(b + S - 1) * tile_bytes);
+      if (b + S - 2 < T)
+        dma16(rv, vdst + slot, vld[i] + (uint32_t)(b + S - 2) * tile_bytes);
     }
+  };
+  // Wait until batch j - S + 2 (issued S - 2 batches before the newest, j)
+  // has landed: vmcnt counts this wave's outstanding DMAs in issue order, so
+  // the wait leaves the newer batches j - S + 3 .. j in flight.
+  auto wait_batch = [&](int j) __attribute__((always_inline)) {
+    int newer = 0;  // DMAs per wave in batches j - S + 3 .. j (wave-uniform)
+#pragma unroll
+    for (int b = j - S + 3; b <= j; ++b) newer += C::LOADS * ((b + S - 1 < T) + (b + S - 2 < T));
+    static_for<0, 2 * (S - 2) * C::LOADS + 1>([&](auto n) __attribute__((always_inline)) {
+      if (newer == decltype(n)::value) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(n)::value) : "memory");
+    });
   };
 
   // MFMA phase: PV of tile j-1 from vsrc (DO_PV) and S^T of tile j from ksrc (DO_QK)
-  auto mfma_phase = [&](auto do_pv, auto do_qk, const char* ksrc, const char* vsrc) __attribute__((always_inline)) {
-    mfma_sequence<D, KB, C::RB, decltype(do_pv)::value, decltype(do_qk)::value>(o, s, l_run, alpha_p, qf, ksrc, vsrc,
+  auto mfma_phase = [&](auto do_pv, auto do_qk, uint32_t ksrc, uint32_t vsrc) __attribute__((always_inline)) {
+    mfma_sequence<D, KB, C::RB, decltype(do_pv)::value, decltype(do_qk)::value>(o, s, qf, ksrc, vsrc,
                                                                                   koff, voff);
   };
 
@@ -330,63 +361,83 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha_p;
     }
-    // P = 2^(S*c - m*c), left in s as float32; the MFMA stage converts it to
-    // bf16 and adds its row sum to l (after l *= alpha_p)
+    // P = 2^(S*c - m*c), left in s as float32 (the MFMA stage converts it to
+    // bf16), and its row sum folded into l
     const float mc = (m_run > kNegInf) ? m_run * c : 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = exp2_sel<EMU16>(__builtin_fmaf(s[kb][e], c, -mc), e);
+    l_run = __builtin_fmaf(l_run, alpha_p, tree_sum<KB>(s));
+    // P and l must be complete here, in the VALU phase. Without these empty
+    // asms the compiler sinks the exponentials into the next MFMA phase, past
+    // the barrier, and the row sum into the VALU phase after it, which keeps
+    // the float32 P of one tile alive next to the S^T of the next (32 more
+    // registers, copied at the loop's back edge).
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(s[kb]));
+    asm volatile("" : "+v"(l_run));
   };
 
   // One step j = [MFMA phase j] barrier [VALU phase j] barrier, identical for
-  // both groups; group 1 runs it one barrier later. Every DMA is issued at
-  // half-phase 2j (group 0 at the start of its MFMA phase j, group 1 at the
-  // start of its VALU phase j-1) and waited for at the end of half-phase 2j+1.
-  // The caller passes the LDS arrays for the parity of j, so every LDS access
-  // has a known target. Step 0 has no PV and step T no S^T or softmax; every
-  // other step runs the full MFMA phase for every wave, also on tiles that the
-  // causal mask empties for some of its rows (the softmax turns those into
-  // P = 0), which keeps the loop free of data-dependent branches.
-  auto step = [&](int j, auto do_pv, auto do_qk, char* kcur, char* knxt, char* vprv, char* vcur)
-      __attribute__((always_inline)) {
-    if (group == 0) load_tiles(j, knxt, vcur);
-    mfma_phase(do_pv, do_qk, kcur, vprv);
-    if (group == 1) wait_own_loads();
+  // both groups; group 1 runs it one barrier later. K_t and V_t sit in ring
+  // slot t % S. DMA batch b (K_{b+S-1}, V_{b+S-2}) is issued at half-phase 2b
+  // (group 0 at the start of its MFMA phase b, group 1 at the start of its
+  // VALU phase b-1), into the slots of K_{b-1} and V_{b-2}, which every wave
+  // finished reading in MFMA phase b-1, and waited for at the end of
+  // half-phase 2b + 2S - 3, just before MFMA phase b+S-1 reads it. The slots
+  // are compile-time constants (the loop is unrolled S times), so every LDS
+  // access has a known target. Step 0 has no PV and step T no S^T or softmax;
+  // every other step runs the full MFMA phase for every wave, also on tiles
+  // that the causal mask empties for some of its rows (the softmax turns those
+  // into P = 0), which keeps the loop free of data-dependent branches.
+  auto kslot = [&](int i) __attribute__((always_inline)) -> char* { return kring + ((i % S + S) % S) * C::TILE; };
+  auto vslot = [&](int i) __attribute__((always_inline)) -> char* { return vring + ((i % S + S) % S) * C::TILE; };
+  auto slot_off = [&](int i) __attribute__((always_inline)) -> uint32_t { return ((i % S + S) % S) * C::TILE; };
+  auto step = [&](int j, auto do_pv, auto do_qk, auto slot) __attribute__((always_inline)) {
+    constexpr int r = decltype(slot)::value;  // j % S
+    if (group == 0) load_tiles(j, kslot(r - 1), vslot(r - 2));
+    mfma_phase(do_pv, do_qk, slot_off(r), slot_off(r - 1));
+    if (group == 1) wait_batch(j);
     block_sync();
-    if (group == 1) load_tiles(j + 1, kcur, vprv);
+    if (group == 1) load_tiles(j + 1, kslot(r), vslot(r - 1));
     if constexpr (decltype(do_qk)::value) valu_phase(j);
-    if (group == 0) wait_own_loads();
+    if (group == 0) wait_batch(j);
     block_sync();
   };
   using Y = std::true_type;
   using N = std::false_type;
+  using I0 = std::integral_constant<int, 0>;
 
-  // prologue: K_0 by every wave
+  // prologue: K_0 .. K_{S-2} and V_0 .. V_{S-3} by every wave
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) dma16(rk, kb0 + 1024 * (wave + 8 * i), kld[i]);
+  for (int t = 0; t < S - 1; ++t)
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int slot = 1024 * (wave + 8 * i);
+      if (t < T) dma16(rk, kring + t * C::TILE + slot, kld[i] + (uint32_t)t * tile_bytes);
+      if (t < S - 2 && t < T) dma16(rv, vring + t * C::TILE + slot, vld[i] + (uint32_t)t * tile_bytes);
+    }
   wait_own_loads();
   block_sync();
   if (group == 1) {
-    // group 1's share of K_1 and V_0 goes out with group 0's, at half-phase 0
-    load_tiles(0, kb1, vb0);
+    // group 1's share of batch 0 goes out with group 0's, at half-phase 0
+    load_tiles(0, kslot(S - 1), vslot(S - 2));
     block_sync();
   }
-  step(0, N{}, Y{}, kb0, kb1, vb1, vb0);
+  step(0, N{}, Y{}, I0{});
   int j = 1;
-  for (; j + 1 < T; j += 2) {
-    step(j, Y{}, Y{}, kb1, kb0, vb0, vb1);
-    step(j + 1, Y{}, Y{}, kb0, kb1, vb1, vb0);
-  }
-  if (j < T) {
-    step(j, Y{}, Y{}, kb1, kb0, vb0, vb1);
-    ++j;
-  }
-  // j == T: PV of the last tile
-  if (j & 1)
-    step(j, Y{}, N{}, kb1, kb0, vb0, vb1);
-  else
-    step(j, Y{}, N{}, kb0, kb1, vb1, vb0);
+  for (; j + S - 1 < T; j += S)
+    static_for<0, S>([&](auto R) __attribute__((always_inline)) {
+      step(j + R, Y{}, Y{}, std::integral_constant<int, (decltype(R)::value + 1) % S>{});
+    });
+  // the remaining steps j .. T-1 (fewer than S; j = 1 mod S), then step T: PV of the last tile
+  static_for<0, S - 1>([&](auto R) __attribute__((always_inline)) {
+    if (j + R < T) step(j + R, Y{}, Y{}, std::integral_constant<int, (decltype(R)::value + 1) % S>{});
+  });
+  static_for<0, S>([&](auto R) __attribute__((always_inline)) {
+    if (T % S == R) step(T, Y{}, N{}, R);
+  });
   if (group == 0) block_sync();
 
   // ---- epilogue: O / l, LSE -------------------------------------------------
