@@ -261,7 +261,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       __builtin_amdgcn_sched_barrier(0);  // keep the update's operand reads below the softmax (registers)
       // element e holds query q0 + 16 (e/8) + 8 h + e%8: two runs of 8 rows,
       // each with its 8 (LSE*log2 e, D) pairs read just before use
-      const bool edge = CAUSAL && q0 + diag < kw0 + 31;
+      if (CAUSAL && q0 + diag < kw0 + 31) {  // masked pairs get S = -inf (one wave-uniform branch)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (key > q0 + 16 * (e >> 3) + 8 * hh + (e & 7) + diag) s[e] = kNegInf;
+      }
       bf16x8 pb[2], db[2];
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
@@ -272,9 +276,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int e = 8 * run + 2 * i + j;
-            float x = __builtin_fmaf(s[e], c, -w[2 * j]);
-            if (edge && key > q0 + 16 * run + 8 * hh + 2 * i + j + diag) x = kNegInf;
-            const float p = exp2_hw(x);
+            const float p = exp2_hw(__builtin_fmaf(s[e], c, -w[2 * j]));
             pb[run][2 * i + j] = (__bf16)p;
             db[run][2 * i + j] = (__bf16)(p * (dp[e] - w[2 * j + 1]));
           }
@@ -396,16 +398,20 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[st], dp, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const bool edge = (CAUSAL && kk0 + 31 > qw0 + diag) || (kk0 + 32 > Nk);
+      // masked keys get S = -inf, in a block of its own behind one
+      // wave-uniform branch (per element, the compiler turns the test into
+      // selects that run on every block)
+      if ((CAUSAL && kk0 + 31 > qw0 + diag) || (kk0 + 32 > Nk)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kj = kk0 + 16 * (e >> 3) + 8 * hh + (e & 7);
+          if (kj >= Nk || (CAUSAL && kj > qi + diag)) s[e] = kNegInf;
+        }
+      }
       bf16x8 db[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float x = __builtin_fmaf(s[e], c, -l2);
-        if (edge) {
-          const int kj = kk0 + 16 * (e >> 3) + 8 * hh + (e & 7);
-          if (kj >= Nk || (CAUSAL && kj > qi + diag)) x = kNegInf;
-        }
-        const float p = exp2_hw(x);
+        const float p = exp2_hw(__builtin_fmaf(s[e], c, -l2));
         db[e >> 3][e & 7] = (__bf16)(p * (dp[e] - dd));
       }
       __builtin_amdgcn_sched_barrier(0);

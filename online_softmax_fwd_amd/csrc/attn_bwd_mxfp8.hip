@@ -353,16 +353,18 @@ void bwd_mx_dkdv_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict
       // element e of lane half h holds query q0 + 32 sb + 16 h + e
       const int qe0 = q0 + 32 * sb + 16 * hh;
       const float4* wp = (const float4*)(wsd + 2 * (32 * sb + 16 * hh));
-      const bool edge = CAUSAL && qe0 - 16 * hh + diag < kw0 + 31;
+      if (CAUSAL && qe0 - 16 * hh + diag < kw0 + 31) {  // masked pairs get S = -inf (one wave-uniform branch)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (key > qe0 + e + diag) s[e] = kNegInf;
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float4 w = wp[i];  // rows 2i, 2i+1 of the lane's 16
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int e = 2 * i + j;
-          float x = __builtin_fmaf(s[e], c, -w[2 * j]);
-          if (edge && key > qe0 + e + diag) x = kNegInf;
-          const float p = exp2_hw(x);
+          const float p = exp2_hw(__builtin_fmaf(s[e], c, -w[2 * j]));
           s[e] = p;
           dp[e] = p * (dp[e] - w[2 * j + 1]);
         }
@@ -515,12 +517,14 @@ void bwd_mx_dq_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
       dp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row_operand(vs, to, kb, 1), gf[1], dp, 0, 0, 2, vsc, 2, gsc);
       // element e of lane half h holds key kk0 + 32 kb + 16 h + e
       const int ke0 = kk0 + 32 * kb + 16 * hh;
-      const bool edge = (CAUSAL && kk0 + 32 * kb + 31 > qw0 + diag) || (kk0 + 32 * kb + 32 > Nk);
+      if ((CAUSAL && kk0 + 32 * kb + 31 > qw0 + diag) || (kk0 + 32 * kb + 32 > Nk)) {  // masked: S = -inf
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (ke0 + e >= Nk || (CAUSAL && ke0 + e > qi + diag)) s[e] = kNegInf;
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float x = __builtin_fmaf(s[e], c, -l2);
-        if (edge && (ke0 + e >= Nk || (CAUSAL && ke0 + e > qi + diag))) x = kNegInf;
-        const float p = exp2_hw(x);
+        const float p = exp2_hw(__builtin_fmaf(s[e], c, -l2));
         dp[e] = p * (dp[e] - dd);
       }
       const uint32_t byte = e8m0_of(wave_absmax(dp));
