@@ -133,10 +133,11 @@ def cpu_baseline(w, causal_modes, flop_budget=1.2e12):
 
 def fwd_kernel_name(w, causal: bool) -> str:
     """The kernel a launch of this workload runs (the bf16 path has a
-    streaming kernel for d = 64 and causal d = 128, a ping-pong kernel for
-    non-causal d = 128)."""
+    ping-pong kernel for d = 128, causal only with at least 256 query tiles of
+    256 rows, and a streaming kernel for everything else)."""
     if w.dtype == "bf16":
-        return "fwd_bf16_stream_kernel" if (w.d != 128 or causal) else "fwd_bf16_kernel"
+        pingpong = w.d == 128 and ((not causal) or w.B * w.H * -(-w.Nq // 256) >= 256)
+        return "fwd_bf16_kernel" if pingpong else "fwd_bf16_stream_kernel"
     return f"fwd_{w.dtype}_kernel"
 
 

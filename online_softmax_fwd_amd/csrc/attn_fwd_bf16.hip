@@ -464,21 +464,21 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
 
 // ---------------------------------------------------------------------------
-// Streaming kernel: d = 64, 192 and 256, and causal d = 128. Each wave owns 32 query rows
+// Streaming kernel: d = 64, 192 and 256, and small causal d = 128 launches. Each wave owns 32 query rows
 // and runs the S^T MFMAs, the softmax and the PV MFMAs of a key tile in
 // order, with no cross-wave phases; K and V tiles stream through two LDS
 // buffers shared by the workgroup. Several workgroups share a CU, so each
 // SIMD interleaves three or four independent streams. Measured against the
 // ping-pong schedule of fwd_bf16_kernel: at d = 64, where the softmax weighs
-// twice as much per MFMA, +17 % non-causal and +23 % causal (B=2, H=32,
-// N=8192); at d = 128 +6 % causal and equal non-causal (B=4, H=16, N=4096),
-// so non-causal d = 128 keeps the ping-pong kernel. The per-tile steps and
-// their sources are those of fwd_bf16_kernel.
+// twice as much per MFMA, 968 vs 883 TFLOP/s non-causal and 898 vs 781
+// causal (B=2, H=32, N=8192); at d = 128 the ping-pong kernel is faster
+// (1137 vs about 1050 non-causal, 1017 vs 987 causal at B=4, H=16, N=4096).
+// The per-tile steps and their sources are those of fwd_bf16_kernel.
 // ---------------------------------------------------------------------------
 // d = 64: 8 waves x 64-key tiles, two workgroups per CU (~120 VGPRs).
 // d = 128: 4 waves x 32-key tiles, three workgroups per CU (~157 VGPRs, 32 KB
-// of LDS each); used for causal launches, where the 128-row workgroups also
-// balance the triangle's uneven work better than 256-row ones.
+// of LDS each); used for causal launches too small to give every CU a
+// 256-row workgroup of the ping-pong kernel.
 // d = 192, 256: 4 waves x 32-key tiles, two workgroups per CU (the O
 // accumulators alone take d/2 VGPRs, Q another d/4; 48 / 64 KB of LDS each).
 template <int D>
@@ -717,12 +717,21 @@ hipError_t launch_k(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// d = 128 runs the ping-pong kernel, except causal launches with fewer than
+// one 256-row workgroup per CU (B * H * ceil(Nq / 256) < 256), where the
+// streaming kernel's 128-row workgroups spread the short launch wider.
+// Measured, causal: B4 H16 N4096 1017 (ping-pong) vs 987 TFLOP/s; B2 H8
+// N1024 31.8 vs 31.2 us.
+constexpr long long kPingPongCausalMinTiles = 256;
 template <int D, bool CAUSAL, int EMU16>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  if constexpr (D != 128 || CAUSAL)
-    return a.cu_q ? launch_stream<D, CAUSAL, EMU16, true>(a, stream) : launch_stream<D, CAUSAL, EMU16, false>(a, stream);
-  else
-    return a.cu_q ? launch_k<D, CAUSAL, EMU16, true>(a, stream) : launch_k<D, CAUSAL, EMU16, false>(a, stream);
+  bool pingpong = D == 128;
+  if (CAUSAL && pingpong) pingpong = (long long)a.B * a.H * ((a.Nq + 255) / 256) >= kPingPongCausalMinTiles;
+  if constexpr (D == 128) {
+    if (pingpong)
+      return a.cu_q ? launch_k<D, CAUSAL, EMU16, true>(a, stream) : launch_k<D, CAUSAL, EMU16, false>(a, stream);
+  }
+  return a.cu_q ? launch_stream<D, CAUSAL, EMU16, true>(a, stream) : launch_stream<D, CAUSAL, EMU16, false>(a, stream);
 }
 
 template <int D, bool CAUSAL>

@@ -221,27 +221,32 @@ def test_device_exp2_matches_model(attn, degree, max_rel):
     assert rel_hw.max() < 1e-6
 
 
-def bf16_key_tile(d, causal):
+def bf16_key_tile(d, causal, B, H, Nq):
     """Keys per tile of the bf16 kernel a launch runs (a lagging-max decision
-    is taken once per tile): the streaming kernel takes 64-key tiles at d = 64
-    and 32-key tiles for causal d = 128; the ping-pong kernel (non-causal
-    d = 128) takes 64-key tiles."""
-    return 32 if (d == 128 and causal) else 64
+    is taken once per tile): the ping-pong kernel (d = 128, causal only with at
+    least 256 query tiles of 256 rows) takes 64-key tiles; the streaming
+    kernel takes 64-key tiles at d = 64 and 32-key tiles at d = 128."""
+    if d == 128:
+        pingpong = (not causal) or B * H * -(-Nq // 256) >= 256
+        return 64 if pingpong else 32
+    return 64
 
 
 @pytest.mark.parametrize("tau", [0.0, 8.0])
-@pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
-def test_rescale_counts_match_oracle(attn, tau, causal, d):
+@pytest.mark.parametrize("causal,d,H", [(False, 64, 2), (True, 64, 2), (False, 128, 2), (True, 128, 2),
+                                        (True, 128, 64)])
+def test_rescale_counts_match_oracle(attn, tau, causal, d, H):
     """The kernel's lagging-max decisions, counted per row and per 32-row
     group, against the oracle's blockwise recurrence at the kernel's key
-    tiles. Near-ties may round differently, so a small slack is allowed."""
+    tiles. Near-ties may round differently, so a small slack is allowed.
+    H = 64 puts causal d = 128 on the ping-pong kernel (256 query tiles of
+    256 rows), H = 2 on the streaming kernel."""
     w = dataclasses.replace(WORKLOADS["bf16_b2h32_n8192_d64_causal_spiky"], d=d)
-    x = make_inputs(w, B=1, H=2, Nq=1024, Nk=2048)
+    x = make_inputs(w, B=1, H=H, Nq=1024, Nk=2048)
     dev = to_device(x)
     _, _, st = attn.fwd_stats(dev["q"], dev["k"], dev["v"], causal=causal, exp2_mode="hw", tau=tau)
-    _, _, ref = blockwise_f64(x["q64"], x["k64"], x["v64"], causal=causal, block=bf16_key_tile(d, causal), tau=tau,
-                              group=32)
+    _, _, ref = blockwise_f64(x["q64"], x["k64"], x["v64"], causal=causal, block=bf16_key_tile(d, causal, 1, H, 1024),
+                              tau=tau, group=32)
     rows_ref, groups_ref = int(ref["rows"].sum()), int(ref["groups"].sum())
     announce(f"d={d} tau={tau} causal={causal}: kernel rescales rows={st[1]} groups={st[3]} "
              f"(steps {st[0]}/{st[2]}); oracle rows={rows_ref} groups={groups_ref}")
