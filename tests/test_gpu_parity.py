@@ -439,12 +439,22 @@ VARLEN_K = [333, 50, 129, 10, 0, 512, 700]
                                   "fp32_b1h1_n128_d64", "bf16_b4h16_n4096_d192", "bf16_b4h16_n4096_d256"])
 @pytest.mark.parametrize("causal", [False, "top_left", "bottom_right"])
 def test_varlen_parity(attn, name, causal):
+    _varlen_check(attn, name, causal, 3)
+
+
+@pytest.mark.parametrize("causal", ["top_left", "bottom_right"])
+def test_varlen_parity_causal_pingpong(attn, causal):
+    """Causal d = 128 takes the ping-pong kernel once the launch has 256 query
+    tiles of 256 rows: 7 sequences x 19 heads x ceil(300 / 256) = 266."""
+    _varlen_check(attn, "bf16_b4h16_n4096_d128", causal, 19)
+
+
+def _varlen_check(attn, name, causal, H):
     import torch
     from attn_inputs import make_packed_inputs
     w = WORKLOADS[name]
-    what = f"{name} packed causal={causal}"
+    what = f"{name} packed causal={causal} H={H}"
     announce(what)
-    H = 3
     x = make_packed_inputs(w, VARLEN_Q, VARLEN_K, H, seed=4242)
     dev = torch.device("cuda", 0)
     if w.dtype == "bf16":
