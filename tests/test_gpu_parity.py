@@ -111,6 +111,28 @@ def test_full_size_sampled_parity(attn, name):
         assert worst_o <= TOL_O[w.dtype] and worst_l <= TOL_LSE
 
 
+@pytest.mark.parametrize("mode", ["hw", "emu", "mix2", "mix8", "emu4", "emu5"])
+def test_causal_pingpong_exp2_modes(attn, mode):
+    """Causal d = 128 on the ping-pong kernel (1 x 64 heads x ceil(1100 / 256)
+    = 320 query tiles of 256 rows) in every exp2 mode, ragged lengths (1100 =
+    17 key tiles of 64 + 12); sampled rows of three heads against the oracle."""
+    w = WORKLOADS["bf16_b4h16_n4096_d128"]
+    x = make_inputs(w, B=1, H=64, Nq=1100, Nk=1100)
+    dev = to_device(x)
+    announce(f"causal ping-pong B=1 H=64 N=1100 mode={mode}")
+    o, lse = run_fwd(attn, dev, True, mode, w.tau)
+    o_h, lse_h = host64(o), host64(lse)
+    rng = np.random.default_rng(7)
+    worst_o = worst_l = 0.0
+    for h in (0, 31, 63):
+        rows = _sample_rows(1100, rng)
+        o_ref, l_ref = attention_rows_f64(x["q64"], x["k64"], x["v64"], 0, h, rows, causal=True)
+        worst_o = max(worst_o, np.abs(o_h[0, h, rows] - o_ref).max())
+        worst_l = max(worst_l, np.abs(lse_h[0, h, rows] - l_ref).max())
+    announce(f"  sampled max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
+    assert np.isfinite(o_h).all() and worst_o <= TOL_O["bf16"] and worst_l <= TOL_LSE
+
+
 @pytest.mark.parametrize("dtype_name", ["fp32_b1h1_n128_d64", "bf16_b2h8_n1024_d128_causal"])
 @pytest.mark.parametrize("shape", [
     (1, 1, 1, 1), (1, 1, 1, 777), (1, 1, 500, 1), (2, 3, 129, 65), (1, 1, 200, 64), (1, 2, 64, 200),
