@@ -133,10 +133,10 @@ def cpu_baseline(w, causal_modes, flop_budget=1.2e12):
 
 def fwd_kernel_name(w, causal: bool) -> str:
     """The kernel a launch of this workload runs (the bf16 path has a
-    ping-pong kernel for d = 128, causal only with at least 256 query tiles of
-    256 rows, and a streaming kernel for everything else)."""
+    ping-pong kernel for d = 128 and 192, causal only with at least 256 query
+    tiles of 256 rows, and a streaming kernel for everything else)."""
     if w.dtype == "bf16":
-        pingpong = w.d == 128 and ((not causal) or w.B * w.H * -(-w.Nq // 256) >= 256)
+        pingpong = w.d in (128, 192) and ((not causal) or w.B * w.H * -(-w.Nq // 256) >= 256)
         return "fwd_bf16_kernel" if pingpong else "fwd_bf16_stream_kernel"
     return f"fwd_{w.dtype}_kernel"
 

@@ -464,7 +464,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
 
 // ---------------------------------------------------------------------------
-// Streaming kernel: d = 64, 192 and 256, and small causal d = 128 launches. Each wave owns 32 query rows
+// Streaming kernel: d = 64 and 256, and small causal d = 128 and 192 launches. Each wave owns 32 query rows
 // and runs the S^T MFMAs, the softmax and the PV MFMAs of a key tile in
 // order, with no cross-wave phases; K and V tiles stream through two LDS
 // buffers shared by the workgroup. Several workgroups share a CU, so each
@@ -480,7 +480,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // of LDS each); used for causal launches too small to give every CU a
 // 256-row workgroup of the ping-pong kernel.
 // d = 192, 256: 4 waves x 32-key tiles, two workgroups per CU (the O
-// accumulators alone take d/2 VGPRs, Q another d/4; 48 / 64 KB of LDS each).
+// accumulators alone take d/2 VGPRs, Q another d/4; 48 / 64 KB of LDS each);
+// d = 192 only for small causal launches.
 template <int D>
 struct StreamCfg : Cfg<D, D == 64 ? 64 : 32, D == 64 ? 8 : 4> {
   static constexpr int WAVES_PER_SIMD = D == 64 ? 4 : D == 128 ? 3 : 2;
@@ -717,17 +718,20 @@ hipError_t launch_k(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// d = 128 runs the ping-pong kernel, except causal launches with fewer than
-// one 256-row workgroup per CU (B * H * ceil(Nq / 256) < 256), where the
-// streaming kernel's 128-row workgroups spread the short launch wider.
-// Measured, causal: B4 H16 N4096 1017 (ping-pong) vs 987 TFLOP/s; B2 H8
-// N1024 31.8 vs 31.2 us.
+// d = 128 and 192 run the ping-pong kernel, except causal launches with
+// fewer than one 256-row workgroup per CU (B * H * ceil(Nq / 256) < 256),
+// where the streaming kernel's 128-row workgroups spread the short launch
+// wider. Measured (B4 H16 N4096, TFLOP/s, ping-pong vs streaming): d = 128
+// 1137 vs ~1050 non-causal, 1017 vs 987 causal; d = 192 1233 vs 1017 and 1078
+// vs 952; causal B2 H8 N1024 d128 31.8 vs 31.2 us. d = 64 stays on the
+// streaming kernel (faster there), d = 256 too (the ping-pong kernel's O and
+// Q operands alone take 192 of its 256 registers).
 constexpr long long kPingPongCausalMinTiles = 256;
 template <int D, bool CAUSAL, int EMU16>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  bool pingpong = D == 128;
+  bool pingpong = D == 128 || D == 192;
   if (CAUSAL && pingpong) pingpong = (long long)a.B * a.H * ((a.Nq + 255) / 256) >= kPingPongCausalMinTiles;
-  if constexpr (D == 128) {
+  if constexpr (D == 128 || D == 192) {
     if (pingpong)
       return a.cu_q ? launch_k<D, CAUSAL, EMU16, true>(a, stream) : launch_k<D, CAUSAL, EMU16, false>(a, stream);
   }

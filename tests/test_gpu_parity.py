@@ -245,13 +245,14 @@ def test_device_exp2_matches_model(attn, degree, max_rel):
 
 def bf16_key_tile(d, causal, B, H, Nq):
     """Keys per tile of the bf16 kernel a launch runs (a lagging-max decision
-    is taken once per tile): the ping-pong kernel (d = 128, causal only with at
-    least 256 query tiles of 256 rows) takes 64-key tiles; the streaming
-    kernel takes 64-key tiles at d = 64 and 32-key tiles at d = 128."""
-    if d == 128:
+    is taken once per tile): the ping-pong kernel (d = 128 and 192, causal
+    only with at least 256 query tiles of 256 rows) takes 64-key tiles; the
+    streaming kernel takes 64-key tiles at d = 64 and 32-key tiles at
+    d = 128, 192 and 256."""
+    if d in (128, 192):
         pingpong = (not causal) or B * H * -(-Nq // 256) >= 256
         return 64 if pingpong else 32
-    return 64
+    return 64 if d == 64 else 32
 
 
 @pytest.mark.parametrize("tau", [0.0, 8.0])
