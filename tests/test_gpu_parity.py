@@ -111,15 +111,17 @@ def test_full_size_sampled_parity(attn, name):
         assert worst_o <= TOL_O[w.dtype] and worst_l <= TOL_LSE
 
 
+@pytest.mark.parametrize("name", ["bf16_b4h16_n4096_d128", "bf16_b4h16_n4096_d192"])
 @pytest.mark.parametrize("mode", ["hw", "emu", "mix2", "mix8", "emu4", "emu5"])
-def test_causal_pingpong_exp2_modes(attn, mode):
-    """Causal d = 128 on the ping-pong kernel (1 x 64 heads x ceil(1100 / 256)
-    = 320 query tiles of 256 rows) in every exp2 mode, ragged lengths (1100 =
-    17 key tiles of 64 + 12); sampled rows of three heads against the oracle."""
-    w = WORKLOADS["bf16_b4h16_n4096_d128"]
+def test_causal_pingpong_exp2_modes(attn, name, mode):
+    """Causal d = 128 and 192 on the ping-pong kernel (1 x 64 heads x
+    ceil(1100 / 256) = 320 query tiles of 256 rows) in every exp2 mode, ragged
+    lengths (1100 = 17 key tiles of 64 + 12); sampled rows of three heads
+    against the oracle."""
+    w = WORKLOADS[name]
     x = make_inputs(w, B=1, H=64, Nq=1100, Nk=1100)
     dev = to_device(x)
-    announce(f"causal ping-pong B=1 H=64 N=1100 mode={mode}")
+    announce(f"causal ping-pong {name} B=1 H=64 N=1100 mode={mode}")
     o, lse = run_fwd(attn, dev, True, mode, w.tau)
     o_h, lse_h = host64(o), host64(lse)
     rng = np.random.default_rng(7)
@@ -465,11 +467,12 @@ def test_varlen_parity(attn, name, causal):
     _varlen_check(attn, name, causal, 3)
 
 
+@pytest.mark.parametrize("name", ["bf16_b4h16_n4096_d128", "bf16_b4h16_n4096_d192"])
 @pytest.mark.parametrize("causal", ["top_left", "bottom_right"])
-def test_varlen_parity_causal_pingpong(attn, causal):
-    """Causal d = 128 takes the ping-pong kernel once the launch has 256 query
-    tiles of 256 rows: 7 sequences x 19 heads x ceil(300 / 256) = 266."""
-    _varlen_check(attn, "bf16_b4h16_n4096_d128", causal, 19)
+def test_varlen_parity_causal_pingpong(attn, name, causal):
+    """Causal d = 128 and 192 take the ping-pong kernel once the launch has 256
+    query tiles of 256 rows: 7 sequences x 19 heads x ceil(300 / 256) = 266."""
+    _varlen_check(attn, name, causal, 19)
 
 
 def _varlen_check(attn, name, causal, H):
