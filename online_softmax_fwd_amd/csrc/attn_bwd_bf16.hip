@@ -73,6 +73,15 @@ __device__ __forceinline__ int swz_dual(int r) {
   return (r & 2) | ((r & 8) >> 1);
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, in order
+template <int B, int E, class F>
+__device__ __forceinline__ void bwd_static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    bwd_static_for<B + 1, E>(f);
+  }
+}
+
 // Per-lane LDS offsets (within a 32-row block of a tile) of the two read
 // patterns, and the global offsets of this lane's DMA chunks.
 template <int D>
@@ -441,6 +450,239 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, c
   if (row_ok) store_row<D>(dQ + qbase + (size_t)qi * D, dq, scale, hh);
 }
 
+// ---------------------------------------------------------------------------
+// dQ on the forward's ping-pong schedule (d = 128): 8 waves x 32 query rows,
+// two groups of 4 (waves i and i+4 share a SIMD), 64-key tiles. Per tile j a
+// wave runs an MFMA phase -- dQ^T += K_{j-1}^T dS_{j-1}^T (16 MFMAs, K^T
+// through the transpose read), then S_j^T = K_j Q^T and dP_j^T = V_j dO^T
+// interleaved (32 MFMAs) -- and a VALU phase: mask, P = 2^(S c - LSE log2 e),
+// dS = P (dP - D), dS to bf16. Group 1 runs one phase behind group 0 with a
+// workgroup barrier between phases, so on every SIMD one wave feeds the
+// matrix core while the other runs the vector work. K is read in two
+// consecutive MFMA phases (S, then dQ), so K and V sit in rings of three
+// tiles; DMA batch b (K_{b+1}, V_{b+1}) is issued at half-phase 2b into the
+// slots of tile b-2, which every wave finished reading in MFMA phase b-1, and
+// waited for at the end of half-phase 2b+1, just before MFMA phase b+1.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                      const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dQ, int Nq,
+                      int Nk, int n_qt, float c, float scale, int bottom_right) {
+  static_assert(D == 128, "the ping-pong dQ kernel is written for d = 128");
+  constexpr int RB = 2 * D, CH = D / 8, NW = 8, BN = 64, KB = BN / 32, TILE = BN * RB, S = 3;
+  constexpr int LOADS = BN * CH / 64 / NW;  // wave-loads per wave per tensor per tile
+  constexpr int NDB = D / 32, NST = D / 16;
+  constexpr int NDQ = NDB * KB * 2, NSP = 2 * KB * NST, RING = 6;
+  __shared__ __attribute__((aligned(1024))) char kring[S * TILE];
+  __shared__ __attribute__((aligned(1024))) char vring[S * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int hh = lane >> 5, l32 = lane & 31;
+
+  int bh, qt;
+  if (CAUSAL) {
+    causal_tile_of(blockIdx.x, gridDim.x, n_qt, bh, qt);
+  } else {
+    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+    bh = logical / n_qt;
+    qt = logical - bh * n_qt;
+  }
+  const int q0 = qt * 32 * NW;
+  const int qw0 = q0 + 32 * wave;
+  const int qi = qw0 + l32;
+  const bool row_ok = qi < Nq;
+  const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const int diag = bottom_right ? Nk - Nq : 0;
+
+  // Per-lane LDS offsets with the ring bases in the register part (opaque to
+  // the compiler, so slot + in-tile offsets fit the 16-bit immediate): K and V
+  // rows for S and dP (permuted rows, one per 16-wide d step), K^T for dQ.
+  uint32_t kr = lds_address(kring), vbase = lds_address(vring);
+  asm volatile("" : "+s"(kr));
+  asm volatile("" : "+s"(vbase));
+  uint32_t rowk[NST], rowv[NST], trk[NDB], ld[LOADS];
+  {
+    const int pr = key_of_row(l32);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const uint32_t o = pr * RB + 16 * ((2 * st + hh) ^ swz_dual<D>(pr));
+      rowk[st] = kr + o;
+      rowv[st] = vbase + o;
+    }
+    const int L = lane & 15, gidx = (lane >> 4) & 1;
+    const int vr = 8 * hh + (L >> 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int cch = 4 * db + 2 * gidx + ((L & 3) >> 1);
+      trk[db] = kr + vr * RB + 16 * (cch ^ swz_dual<D>(vr)) + 8 * (L & 1);
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int pos = 64 * (wave + NW * i) + lane;
+      const int r = pos / CH, p = pos % CH;
+      ld[i] = r * RB + 16 * (p ^ swz_dual<D>(r));
+    }
+  }
+  const u32x4 rk = raw_buffer_rsrc(K + kbase, (uint32_t)(Nk * RB));
+  const u32x4 rv = raw_buffer_rsrc(V + kbase, (uint32_t)(Nk * RB));
+
+  bf16x8 qf[NST], gf[NST];
+  load_row_operand<D>(qf, Q + qbase + (size_t)(row_ok ? qi : 0) * D, row_ok, hh);
+  load_row_operand<D>(gf, dO + qbase + (size_t)(row_ok ? qi : 0) * D, row_ok, hh);
+  float l2 = -kNegInf, dd = 0.0f;  // rows past Nq: P = 0
+  if (row_ok) {
+    const float2 w = *(const float2*)(ws + ((size_t)bh * Nq + qi) * 2);
+    l2 = w[0];
+    dd = w[1];
+  }
+
+  floatx16 dq[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dq[i] = floatx16{};
+  const int kend = CAUSAL ? min(Nk, q0 + 32 * NW + diag) : Nk;
+  const int T = kend > 0 ? (kend + BN - 1) / BN : 0;
+  if (T == 0) {  // no row of this workgroup sees a key: dQ = 0
+    if (row_ok) store_row<D>(dQ + qbase + (size_t)qi * D, dq, scale, hh);
+    return;
+  }
+
+  floatx16 s[KB], dp[KB];  // S^T and dP^T of the current tile
+  bf16x8 db[KB][2];        // dS^T of the previous tile, the dQ MFMAs' B operand
+
+  auto slot_off = [&](int i) __attribute__((always_inline)) -> uint32_t { return ((i % S + S) % S) * TILE; };
+  // DMA batch b: this wave's share of K_{b+1} and V_{b+1}
+  auto load_tiles = [&](int b) __attribute__((always_inline)) {
+    if (b + 1 < T) {
+      const uint32_t so = slot_off(b + 1), go = (uint32_t)(b + 1) * TILE;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        dma16(rk, kring + so + 1024 * (wave + NW * i), ld[i] + go);
+        dma16(rv, vring + so + 1024 * (wave + NW * i), ld[i] + go);
+      }
+    }
+  };
+
+  // MFMA phase: dQ of tile j-1 (K^T from kprev), then S^T and dP^T of tile j
+  // (K and V rows from kcur / vcur), operands read RING MFMAs ahead
+  auto mfma_phase = [&](auto do_dq, auto do_sp, uint32_t kprev, uint32_t kcur, uint32_t vcur)
+      __attribute__((always_inline)) {
+    constexpr int N0 = decltype(do_dq)::value ? NDQ : 0;
+    constexpr int N = N0 + (decltype(do_sp)::value ? NSP : 0);
+    auto read = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      if (i < N0) {
+        const int d = i % NDB, k = i / NDB, kb = k >> 1, cc = k & 1;
+        const uint32_t p = trk[d] + kprev + (32 * kb + 16 * cc) * RB;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(uintptr_t)(p));
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(uintptr_t)(p + 4 * RB));
+        return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                                __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+      }
+      const int q = i - N0, dpk = q & 1, kb = (q >> 1) & 1, st = q >> 2;
+      const uint32_t p = (dpk ? rowv[st] + vcur : rowk[st] + kcur) + kb * 32 * RB;
+      return *(const lds_bf16x8*)(uintptr_t)(p);
+    };
+    bf16x8 ring[RING];
+#pragma unroll
+    for (int i = 0; i < RING && i < N; ++i) ring[i] = read(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const bf16x8 a = ring[i % RING];
+      if (i + RING < N) ring[i % RING] = read(i + RING);
+      if (i < N0) {
+        const int d = i % NDB, k = i / NDB, kb = k >> 1, cc = k & 1;
+        dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, db[kb][cc], dq[d], 0, 0, 0);
+      } else {
+        const int q = i - N0, dpk = q & 1, kb = (q >> 1) & 1, st = q >> 2;
+        if (dpk)
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[st], st == 0 ? floatx16{} : dp[kb], 0, 0, 0);
+        else
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? floatx16{} : s[kb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // VALU phase j: masked keys get S = -inf (one wave-uniform branch per 32-key
+  // block), P, dS, and dS^T as bf16 for the next MFMA phase
+  auto valu_phase = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int kk0 = j * BN + 32 * kb;
+      if ((CAUSAL && kk0 + 31 > qw0 + diag) || (kk0 + 32 > Nk)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kj = kk0 + 16 * (e >> 3) + 8 * hh + (e & 7);
+          if (kj >= Nk || (CAUSAL && kj > qi + diag)) s[kb][e] = kNegInf;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2_hw(__builtin_fmaf(s[kb][e], c, -l2));
+        db[kb][e >> 3][e & 7] = (__bf16)(p * (dp[kb][e] - dd));
+      }
+    }
+    // dS must be complete here, in the VALU phase (the compiler would sink it
+    // into the next MFMA phase, past the barrier)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) asm volatile("" : "+v"(db[kb][cc]));
+  };
+
+  // One step j = [MFMA phase j] barrier [VALU phase j] barrier; group 1 runs
+  // it one barrier later. Batch j goes out at half-phase 2j (group 0 at the
+  // start of its MFMA phase j, group 1 at the start of its VALU phase j-1)
+  // and every wave waits for its share at the end of half-phase 2j+1.
+  auto step = [&](int j, auto do_dq, auto do_sp, auto slot) __attribute__((always_inline)) {
+    constexpr int r = decltype(slot)::value;  // j % S
+    if (group == 0) load_tiles(j);
+    mfma_phase(do_dq, do_sp, slot_off(r - 1), slot_off(r), slot_off(r));
+    if (group == 1) wait_own_loads();
+    block_sync();
+    if (group == 1) load_tiles(j + 1);
+    if constexpr (decltype(do_sp)::value) valu_phase(j);
+    if (group == 0) wait_own_loads();
+    block_sync();
+  };
+  using Y = std::true_type;
+  using N = std::false_type;
+
+  // prologue: K_0 and V_0 by every wave; group 1's share of batch 0 (K_1, V_1)
+  // goes out with group 0's, at half-phase 0
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    dma16(rk, kring + 1024 * (wave + NW * i), ld[i]);
+    dma16(rv, vring + 1024 * (wave + NW * i), ld[i]);
+  }
+  wait_own_loads();
+  block_sync();
+  if (group == 1) {
+    load_tiles(0);
+    block_sync();
+  }
+  step(0, N{}, Y{}, std::integral_constant<int, 0>{});
+  int j = 1;
+  for (; j + S - 1 < T; j += S)
+    bwd_static_for<0, S>([&](auto R) __attribute__((always_inline)) {
+      step(j + R, Y{}, Y{}, std::integral_constant<int, (decltype(R)::value + 1) % S>{});
+    });
+  // the remaining steps j .. T-1 (fewer than S; j = 1 mod S), then step T: dQ of the last tile
+  bwd_static_for<0, S - 1>([&](auto R) __attribute__((always_inline)) {
+    if (j + R < T) step(j + R, Y{}, Y{}, std::integral_constant<int, (decltype(R)::value + 1) % S>{});
+  });
+  bwd_static_for<0, S>([&](auto R) __attribute__((always_inline)) {
+    if (T % S == R) step(T, Y{}, N{}, R);
+  });
+  if (group == 0) block_sync();
+
+  if (row_ok) store_row<D>(dQ + qbase + (size_t)qi * D, dq, scale, hh);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   using C = BwdCfg<D>;
@@ -459,6 +701,17 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
                        (const __bf16*)a.d_o, (const float*)a.ws, (__bf16*)a.d_k, (__bf16*)a.d_v, a.Nq, a.Nk, n_kt,
                        a.scale_log2, a.scale, a.bottom_right);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if constexpr (D == 128) {
+    const int n_qt = (a.Nq + 255) / 256;
+    if (n_qt > 0) {
+      hipLaunchKernelGGL((bwd_dq_pp_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.B * a.H * n_qt)), dim3(512), 0,
+                         stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.d_o,
+                         (const float*)a.ws, (__bf16*)a.d_q, a.Nq, a.Nk, n_qt, a.scale_log2, a.scale,
+                         a.bottom_right);
+      e = hipGetLastError();
+    }
+    return e;
   }
   const int n_qt = (a.Nq + 32 * C::NW - 1) / (32 * C::NW);
   if (n_qt > 0) {

@@ -111,8 +111,8 @@ def _run_case(attn, d, B, H, Nq, Nk, causal, source, seed=7):
 @pytest.mark.parametrize("causal", [False, "top_left", "bottom_right"])
 @pytest.mark.parametrize("source", ["oracle", "kernel"])
 def test_bwd_small_ragged(attn, d, causal, source):
-    """Several tiles with ragged tails on both sides (query tiles of 64 and
-    128 rows, key blocks of 128 and tiles of 64)."""
+    """Several tiles with ragged tails on both sides (query tiles of 64, 128
+    and 256 rows, key blocks of 128 and tiles of 64)."""
     announce(f"bwd small d={d} causal={causal} {source}")
     _run_case(attn, d, 1, 2, 300, 333, causal, source)
 
@@ -120,10 +120,12 @@ def test_bwd_small_ragged(attn, d, causal, source):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("nq,nk,causal", [(100, 333, "bottom_right"), (333, 100, "bottom_right"),
                                           (333, 100, "top_left"), (1, 300, False), (300, 1, False),
-                                          (1, 1, "top_left"), (64, 64, "top_left"), (129, 257, False)])
+                                          (1, 1, "top_left"), (64, 64, "top_left"), (129, 257, False),
+                                          (600, 100, "bottom_right")])
 def test_bwd_edge_shapes(attn, d, nq, nk, causal):
     """Nq != Nk both ways (bottom-right with Nq > Nk leaves rows without keys:
-    their dQ is 0 and they add nothing), single rows and keys, exact tiles."""
+    their dQ is 0 and they add nothing; at 600 x 100 whole 256-row dQ
+    workgroups see no key), single rows and keys, exact tiles."""
     announce(f"bwd edge d={d} Nq={nq} Nk={nk} causal={causal}")
     _run_case(attn, d, 1, 2, nq, nk, causal, "oracle", seed=nq + 7 * nk)
 
