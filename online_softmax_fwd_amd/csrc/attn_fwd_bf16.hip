@@ -111,14 +111,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // previous tile, then the S^T MFMAs of the current tile. Operands come from
 // LDS through a ring RING MFMAs deep (the LDS round trip is several MFMA
 // durations long), and consecutive MFMAs rotate over independent accumulators
-// (the 4 (d=128) or 2 (d=64) blocks of O^T, then the 2 blocks of S^T).
-// While the first operands are in flight the wave converts the previous
-// tile's float32 P (left in s by the softmax stage) to bf16.
+// (the 4 (d=128) or 2 (d=64) blocks of O^T, then the 2 blocks of S^T). The
+// previous tile's P arrives as bf16 (pb, converted by the softmax stage).
 // sched_barrier pins the issue order so the reads stay ahead.
 // ---------------------------------------------------------------------------
 template <int D, int KB, int RB, bool DO_PV, bool DO_QK>
-__device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&s)[KB], const bf16x8 (&qf)[D / 16],
-                                              uint32_t ksrc, uint32_t vsrc,
+__device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&s)[KB], const bf16x8 (&pb)[KB][2],
+                                              const bf16x8 (&qf)[D / 16], uint32_t ksrc, uint32_t vsrc,
                                               const uint32_t (&koff)[D / 16], const uint32_t (&voff)[D / 32]) {
   constexpr int NDB = D / 32;
   constexpr int NPV = DO_PV ? NDB * KB * 2 : 0;
@@ -141,15 +140,6 @@ __device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&
 #pragma unroll
   for (int i = 0; i < RING && i < N; ++i) ring[i] = read(i);
 
-  bf16x8 pb[KB][2];
-  if constexpr (DO_PV) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[kb][cc][e] = (__bf16)s[kb][8 * cc + e];
-  }
   __builtin_amdgcn_sched_barrier(0);
 
   auto mma = [&](int i, const bf16x8& a) __attribute__((always_inline)) {
@@ -293,6 +283,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = floatx16{};
   floatx16 s[KB];        // S^T of the current tile, then its float32 P
+  bf16x8 pb[KB][2];      // that P as bf16, the next MFMA phase's PV B operand
   float alpha_p = 1.0f;  // rescale factor of the tile whose P is in s
   float m_run = kNegInf;  // running max, raw score units
   float l_run = 0.0f;     // running denominator over this lane's half of the keys
@@ -322,10 +313,20 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     });
   };
 
-  // MFMA phase: PV of tile j-1 from vsrc (DO_PV) and S^T of tile j from ksrc (DO_QK)
+  // MFMA phase: PV of tile j-1 from vsrc (DO_PV) and S^T of tile j from ksrc
+  // (DO_QK). The MFMA phase sets the pace of the schedule (more MFMA work per
+  // tile costs more than less softmax work saves), so a wave raises its issue
+  // priority while in it: when the matrix core frees up, the SIMD issues the
+  // next MFMA before the other wave's vector instructions.
   auto mfma_phase = [&](auto do_pv, auto do_qk, uint32_t ksrc, uint32_t vsrc) __attribute__((always_inline)) {
-    mfma_sequence<D, KB, C::RB, decltype(do_pv)::value, decltype(do_qk)::value>(o, s, qf, ksrc, vsrc,
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_sequence<D, KB, C::RB, decltype(do_pv)::value, decltype(do_qk)::value>(o, s, pb, qf, ksrc, vsrc,
                                                                                   koff, voff);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // VALU phase j: softmax of tile j
@@ -361,21 +362,31 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha_p;
     }
-    // P = 2^(S*c - m*c), left in s as float32 (the MFMA stage converts it to
-    // bf16), and its row sum folded into l
+    // P = 2^(S*c - m*c) as float32 in s, its row sum folded into l, and P as
+    // bf16 in pb (converted here rather than at the start of the MFMA phase,
+    // which is the critical one; this also carries 16 registers of P across
+    // the barrier instead of 32)
     const float mc = (m_run > kNegInf) ? m_run * c : 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = exp2_sel<EMU16>(__builtin_fmaf(s[kb][e], c, -mc), e);
     l_run = __builtin_fmaf(l_run, alpha_p, tree_sum<KB>(s));
-    // P and l must be complete here, in the VALU phase. Without these empty
-    // asms the compiler sinks the exponentials into the next MFMA phase, past
-    // the barrier, and the row sum into the VALU phase after it, which keeps
-    // the float32 P of one tile alive next to the S^T of the next (32 more
-    // registers, copied at the loop's back edge).
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(s[kb]));
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[kb][cc][e] = (__bf16)s[kb][8 * cc + e];
+    // P and l must be complete here, in the VALU phase. Without these empty
+    // asms the compiler sinks the exponentials and the conversion into the
+    // next MFMA phase, past the barrier, and the row sum into the VALU phase
+    // after it, which keeps the float32 P of one tile alive next to the S^T of
+    // the next (32 more registers, copied at the loop's back edge).
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) asm volatile("" : "+v"(pb[kb][cc]));
     asm volatile("" : "+v"(l_run));
   };
 
