@@ -702,16 +702,20 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
                        a.scale_log2, a.scale, a.bottom_right);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // The ping-pong dQ kernel takes 256 query rows per workgroup and fills a CU
+  // with one. Below one workgroup per CU the streaming kernel, with twice as
+  // many 128-row workgroups, finishes first (whole backward, B2 H8 N1024
+  // causal: 125 against 117 TFLOP/s; B1 H4 N2048: 130 against 127).
+  constexpr long long kDqPingPongMinTiles = 256;
   if constexpr (D == 128) {
     const int n_qt = (a.Nq + 255) / 256;
-    if (n_qt > 0) {
+    if (n_qt > 0 && (long long)a.B * a.H * n_qt >= kDqPingPongMinTiles) {
       hipLaunchKernelGGL((bwd_dq_pp_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.B * a.H * n_qt)), dim3(512), 0,
                          stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.d_o,
                          (const float*)a.ws, (__bf16*)a.d_q, a.Nq, a.Nk, n_qt, a.scale_log2, a.scale,
                          a.bottom_right);
-      e = hipGetLastError();
+      return hipGetLastError();
     }
-    return e;
   }
   const int n_qt = (a.Nq + 32 * C::NW - 1) / (32 * C::NW);
   if (n_qt > 0) {

@@ -130,6 +130,23 @@ def test_bwd_edge_shapes(attn, d, nq, nk, causal):
     _run_case(attn, d, 1, 2, nq, nk, causal, "oracle", seed=nq + 7 * nk)
 
 
+# d = 128 launches with B*H*ceil(Nq/256) >= 256 take the ping-pong dQ kernel
+# (256 query rows per workgroup); smaller ones the streaming dQ kernel.
+DQ_PINGPONG_MIN_TILES = 256
+
+
+@pytest.mark.parametrize("nq,nk,causal", [(300, 333, False), (300, 333, "top_left"), (300, 333, "bottom_right"),
+                                          (600, 100, "bottom_right"), (1100, 1030, "top_left")])
+def test_bwd_pingpong_dq(attn, nq, nk, causal):
+    """Enough heads for the ping-pong dQ kernel, every element: ragged query
+    and key tails, 1 to 17 key tiles per workgroup (every count mod 3, the
+    kernel's unroll), workgroups that see no key (bottom-right 600 x 100)."""
+    n_qt = -(-nq // 256)
+    H = -(-DQ_PINGPONG_MIN_TILES // n_qt)
+    announce(f"bwd ping-pong dQ d=128 H={H} Nq={nq} Nk={nk} causal={causal}")
+    _run_case(attn, 128, 1, H, nq, nk, causal, "oracle", seed=nq + 3 * nk)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_larger_heads(attn, d):
     """B=2, H=3 at 1024 x 1024 (a causal triangle of 16 query tiles), every element."""
