@@ -29,6 +29,11 @@
 //                     64-key tiles like the forward kernel:
 //                       S^T  = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - D)
 //                       dQ^T += K^T dS^T    A = K^T (LDS transpose read)
+//   bwd_dq_pp_kernel  the same products on the forward's ping-pong schedule
+//                     (d = 128, 256 queries per workgroup, two groups of 4
+//                     waves alternating MFMA and vector phases); it serves
+//                     launches with at least one workgroup per CU, the
+//                     streaming kernel the smaller ones and d = 64.
 //
 // dQ has its own kernel (recomputing S and dP: seven products instead of
 // five) rather than atomic float adds from every key block into a float32
