@@ -66,7 +66,7 @@ def test_exact_values(degree):
 @pytest.mark.parametrize("degree", [4, 5])
 def test_model_uses_the_fitted_coefficients(degree):
     src = open(os.path.join(os.path.dirname(HERE), "oracle", "ex2_emu.c")).read()
-    table = re.search(rf"kQ{degree}\[{degree + 1}\] = \{{(.*?)\}};", src, flags=re.S).group(1)
+    table = re.search(rf"kDeg{degree}\[{degree + 1}\] = \{{(.*?)\}};", src, flags=re.S).group(1)
     committed = np.array([float(t.strip().rstrip("f")) for t in table.split(",")], dtype=np.float32)
     fitted = fit_ex2_poly(degree)
     # the same float32 values (at most 2 float32 steps apart on another BLAS)
