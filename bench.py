@@ -83,6 +83,9 @@ def parse():
     p.add_argument("--tau", type=float, default=None)
     p.add_argument("--fp8-p", default="block", choices=["block", "e4m3", "e5m2"],
                    help="MXFP8 workloads: P scaled per 32-key block, or times 2^8 with one fixed scale as E4M3 or E5M2")
+    p.add_argument("--no-split", action="store_true",
+                   help="run every launch whole (attn_fwd_ex) instead of letting the library cut small launches "
+                        "into key chunks (attn_fwd_split)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bwd", action="store_true", help="skip the backward-pass section")
     p.add_argument("--bwd-steps", type=int, default=50)
@@ -90,6 +93,27 @@ def parse():
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (HBM counter calibration)")
     return p.parse_args()
+
+
+def metric_of(w) -> str:
+    """The metric's name for a workload: dtype, head dim, length and the
+    causal settings one step runs."""
+    causal = "causal & non" if len(w.causal) == 2 else ("causal" if w.causal[0] else "non-causal")
+    n = f"N={w.Nq}" if w.Nq == w.Nk else f"Nq={w.Nq} Nk={w.Nk}"
+    return f"attn fwd TFLOP/s, {w.dtype} d={w.d} {n} ({causal}), % of MFMA peak"
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 def flops_of(w, causal: bool) -> float:
@@ -126,15 +150,20 @@ def cpu_baseline(w, causal_modes, flop_budget=1.2e12):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{what}, Nq=Nk={w.Nq} d={w.d}, causal modes {list(causal_modes)}; float64 numpy one-shot "
-                  f"softmax (it forms the full S even when causal; FLOPs counted as for the GPU); {dt:.1f} s",
+                  f"softmax (it forms the full S even when causal; FLOPs counted as for the GPU); {dt:.1f} s on "
+                  f"{threads} BLAS threads of {len(os.sched_getaffinity(0))} usable cores, {cpu_model()}",
+        "cpu_model": cpu_model(),
         "seconds": round(dt, 2),
     }
 
 
-def fwd_kernel_name(w, causal: bool) -> str:
+def fwd_kernel_name(w, causal: bool, split: bool = False) -> str:
     """The kernel a launch of this workload runs (the bf16 path has a
     ping-pong kernel for d = 128 and 192, causal only with at least 256 query
-    tiles of 256 rows, and a streaming kernel for everything else)."""
+    tiles of 256 rows, and a streaming kernel for everything else; a split
+    launch runs the streaming kernel over key chunks, then a merge kernel)."""
+    if split:
+        return "fwd_bf16_stream_kernel (key chunks) + fwd_split_merge_kernel"
     if w.dtype == "bf16":
         pingpong = w.d in (128, 192) and ((not causal) or w.B * w.H * -(-w.Nq // 256) >= 256)
         return "fwd_bf16_kernel" if pingpong else "fwd_bf16_stream_kernel"
@@ -223,10 +252,20 @@ def main():
     outs = {c: (torch.empty((w.B, w.H, w.Nq, w.d), dtype=odt, device=dev),
                 torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)) for c in w.causal}
     stream = torch.cuda.current_stream(dev)
+    # key-split workspaces (allocated before timing; none when the library
+    # runs a launch whole, as it does for launches that fill the chip)
+    ws = {}
+    for c in w.causal:
+        n = 0 if args.no_split else attn.split_workspace_bytes(q, k, causal=c, fp8_p=args.fp8_p)
+        ws[c] = torch.empty(-(-n // 4), dtype=torch.float32, device=dev) if n > 0 else None
 
     def launch(causal):
         o, l = outs[causal]
-        attn.fwd(q, k, v, causal=causal, exp2_mode=mode, tau=tau, out=o, lse=l, stream=stream, **scales, **fp8)
+        if args.no_split:
+            attn.fwd(q, k, v, causal=causal, exp2_mode=mode, tau=tau, out=o, lse=l, stream=stream, **scales, **fp8)
+        else:
+            attn.fwd_split(q, k, v, causal=causal, exp2_mode=mode, tau=tau, out=o, lse=l, stream=stream,
+                           workspace=ws[causal], **scales, **fp8)
 
     for _ in range(args.warmup):
         for c in w.causal:
@@ -276,7 +315,7 @@ def main():
         mix16 = {("causal" if c else "noncausal"): lib.attn_mix_sixteenths(dcode, w.d, int(c)) for c in w.causal}
 
     result = {
-        "metric": "attn fwd TFLOP/s, bf16 d=128 N=4096 (causal & non), % of MFMA peak",
+        "metric": metric_of(w),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -294,13 +333,15 @@ def main():
                         f"exp2 {mode}, tau={tau}",
             "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": list(w.causal),
             "exp2_mode": mode, "mix_sixteenths": mix16, "tau": tau, "seed": w.seed,
+            "key_split": {("causal" if c else "noncausal"): (ws[c] is not None) for c in w.causal},
             **({"fp8_p": args.fp8_p} if w.dtype == "mxfp8" else {}),
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
         "per_mode": per_mode,
         "roofline": {
             "bound": "mfma",
-            "kernel": f"{fwd_kernel_name(w, dom)} (d={w.d}, {'causal' if dom else 'non-causal'})",
+            "kernel": f"{fwd_kernel_name(w, dom, ws[dom] is not None)} (d={w.d}, "
+                      f"{'causal' if dom else 'non-causal'})",
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": "TFLOP/s",

@@ -48,8 +48,8 @@ enum {
                             (Nq or Nk above 2^30, or one (b, h) slice of Q, K or V
                             of 2 GiB or more); MXFP8 with Nq or Nk not a
                             multiple of 32                                            */
-  ATTN_E_HEADDIM = -3,   /* d not supported for the dtype (f32/bf16: 64 or 128;
-                            MXFP8: 128)                                                */
+  ATTN_E_HEADDIM = -3,   /* d not supported for the dtype (bf16: 64, 128, 192 or
+                            256; f32: 64 or 128; MXFP8: 128)                           */
   ATTN_E_DTYPE = -4,     /* unknown dtype code                                         */
   ATTN_E_EXP2MODE = -5,  /* unknown exp2_mode                                          */
   ATTN_E_TAU = -6,       /* tau negative, above 64 or not finite; for the fixed-scale
@@ -122,7 +122,7 @@ enum {
  *             scaled scores of each row
  *   B, H, Nq  >= 0 (a zero means there is nothing to do: returns ATTN_OK)
  *   Nk        >= 1 when B*H*Nq > 0
- *   d         64 or 128
+ *   d         64, 128, 192 or 256
  *   causal    0 = no mask; 1 = causal aligned top-left: key j is removed for
  *             query i when j > i ("Lecture 2 -- Online Softmax and Numerical
  *             Correctness", section "Causal masking just changes which blocks
@@ -163,6 +163,60 @@ int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE
                 int exp2_mode, float tau, int dtype,
                 const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
                 void* stream);
+
+/*
+ * attn_fwd_split_workspace_bytes -- bytes of float32 workspace attn_fwd_split
+ * needs for this launch: 0 when the launch is not split (dtype other than
+ * ATTN_BF16, nothing to compute, or key_chunk = 0 and the library runs the
+ * launch whole); -1 when the sizes or key_chunk are invalid (as attn_fwd_ex
+ * would reject them).
+ */
+long long attn_fwd_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, int causal,
+                                         int dtype, int key_chunk);
+
+/*
+ * attn_fwd_split -- attn_fwd_ex that may cut each row's keys into chunks run
+ * by separate workgroups, for launches with too few query tiles to fill the
+ * GPU (small batches, few heads, decoding-like Nq << Nk).
+ *
+ * Source: "Lecture 2 -- Online Softmax and Numerical Correctness", section
+ * "Combining two blocks exactly": the softmax states (max, denominator,
+ * output) of two key ranges combine exactly into the state of their union,
+ * so a row may be computed chunk by chunk anywhere and merged afterwards.
+ * Each chunk's workgroup writes its normalised float32 output O_k and its
+ * log-sum-exp L_k (log2 units) to the workspace; a second kernel forms
+ * L = max L_k, w_k = 2^(L_k - L), O = sum w_k O_k / sum w_k and
+ * LSE = ln2 * (L + log2 sum w_k). Query tiles whose keys fit one chunk are
+ * written directly.
+ *
+ *   Q .. stream   as attn_fwd_ex (all dtypes; only ATTN_BF16 dense launches
+ *                 are split, every other launch runs as attn_fwd_ex and
+ *                 needs no workspace)
+ *   key_chunk     0: the library's choice: a launch is split when run whole
+ *                 it would occupy fewer than a quarter of the compute units
+ *                 (decoding-like shapes, few heads), into chunks of at least
+ *                 128 keys sized for two workgroups per compute unit; larger
+ *                 launches run whole (measured: splitting gains nothing there,
+ *                 the partials' memory traffic costs what the shorter chains
+ *                 save);
+ *                 > 0: a multiple of 64, keys per chunk (bf16 launches are
+ *                 then always run by the split kernels)
+ *   workspace     device memory of >= attn_fwd_split_workspace_bytes(...)
+ *                 bytes, 16-byte aligned, owned by the caller (NULL allowed
+ *                 when that size is 0); contents on entry are ignored and
+ *                 nothing in it needs to start at zero. Calls that share a
+ *                 workspace must not overlap.
+ *   workspace_bytes  its size
+ * Exp2 modes, tau and the causal settings are those of attn_fwd_ex; the
+ * rescale decisions of the lagging max are taken per chunk. Errors: those of
+ * attn_fwd_ex; ATTN_E_SHAPE for a bad key_chunk or a workspace that is too
+ * small, ATTN_E_NULLPTR / ATTN_E_ALIGN for a missing or unaligned workspace.
+ */
+int attn_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                   int exp2_mode, float tau, int dtype,
+                   const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                   int key_chunk, float* workspace, long long workspace_bytes, void* stream);
 
 /*
  * attn_fwd_varlen -- a batch of sequences of different lengths, packed.

@@ -21,7 +21,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_varlen", "fwd_stats", "bwd", "mx_quantize", "mx_scale_offsets", "mx_scale_scatter", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
+__all__ = ["fwd", "fwd_split", "split_workspace_bytes", "fwd_varlen", "fwd_stats", "bwd", "mx_quantize", "mx_scale_offsets", "mx_scale_scatter", "exp2", "mix_sixteenths", "AttnError", "lib_path", "load_library",
            "ATTN_F32", "ATTN_BF16", "ATTN_MXFP8_E4M3", "ATTN_MXFP8_E4M3_PFIX_E4M3", "ATTN_MXFP8_E4M3_PFIX_E5M2",
            "EXP2_MODES", "STATUS"]
 
@@ -63,6 +63,10 @@ def load_library():
     lib.attn_fwd_ex.argtypes = fwd_args + [ci, vp, vp, vp, vp]
     lib.attn_fwd_ex.restype = ci
     lib.attn_fwd_stats.argtypes = fwd_args + [ci, vp, vp, vp, vp, vp]
+    lib.attn_fwd_split_workspace_bytes.argtypes = [ci] * 8
+    lib.attn_fwd_split_workspace_bytes.restype = ctypes.c_longlong
+    lib.attn_fwd_split.argtypes = fwd_args + [ci, vp, vp, vp, ci, vp, ctypes.c_longlong, vp]
+    lib.attn_fwd_split.restype = ci
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, cf, ci, vp]
     lib.attn_fwd_varlen.restype = ci
     lib.attn_fwd_varlen_ex.argtypes = [vp] * 12 + [ci] * 9 + [cf, ci, cf, ci, vp]
@@ -175,6 +179,43 @@ def fwd(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 
     _check(lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                            B, H, Nq, k.shape[2], d, _causal(causal), scale, _mode(exp2_mode), float(tau),
                            dtype, scales[0], scales[1], scales[2], _stream_ptr(stream, q.device)))
+    return out, lse
+
+
+def split_workspace_bytes(q, k, causal=False, key_chunk: int = 0, fp8_p="block") -> int:
+    """Workspace bytes attn_fwd_split needs for these tensors (0: not split)."""
+    import torch
+    lib = load_library()
+    B, H, Nq, d = q.shape
+    dtype = ATTN_F32 if q.dtype == torch.float32 else ATTN_BF16 if q.dtype == torch.bfloat16 else FP8_P[fp8_p]
+    n = int(lib.attn_fwd_split_workspace_bytes(B, H, Nq, k.shape[2], d, _causal(causal), dtype, int(key_chunk)))
+    if n < 0:
+        raise AttnError(-2, lib.attn_last_error().decode())
+    return n
+
+
+def fwd_split(q, k, v, causal: bool = False, scale=None, exp2_mode="hw", tau: float = 8.0, out=None, lse=None,
+              q_scale=None, k_scale=None, v_scale=None, stream=None, fp8_p="block", key_chunk: int = 0,
+              workspace=None):
+    """fwd through attn_fwd_split: launches with too few query tiles to fill
+    the GPU are cut into key chunks run by separate workgroups and merged
+    exactly. key_chunk 0 lets the library choose (no split for large
+    launches); a positive multiple of 64 forces that chunk (bf16). The float32
+    workspace is allocated here unless given. Returns (O, LSE)."""
+    import torch
+    lib = load_library()
+    dtype, out, lse, scales = _prepare(q, k, v, out, lse, q_scale, k_scale, v_scale, fp8_p)
+    B, H, Nq, d = q.shape
+    nbytes = split_workspace_bytes(q, k, causal, key_chunk, fp8_p)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(-(-nbytes // 4), dtype=torch.float32, device=q.device)
+    wptr, wbytes = (0, 0) if workspace is None else (workspace.data_ptr(),
+                                                      workspace.numel() * workspace.element_size())
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              B, H, Nq, k.shape[2], d, _causal(causal), scale, _mode(exp2_mode), float(tau),
+                              dtype, scales[0], scales[1], scales[2], int(key_chunk), wptr, wbytes,
+                              _stream_ptr(stream, q.device)))
     return out, lse
 
 

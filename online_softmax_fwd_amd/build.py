@@ -26,6 +26,7 @@ SOURCES = [
     "attn_api.cpp",
     "attn_exp2.hip",
     "attn_fwd_bf16.hip",
+    "attn_fwd_bf16_split.hip",
     "attn_fwd_f32.hip",
     "attn_fwd_mxfp8.hip",
     "attn_mx_layout.hip",

@@ -186,6 +186,26 @@ int run(const attn::FwdArgs& a, int dtype, void* stream) {
   return ATTN_OK;
 }
 
+// Shared by attn_fwd_split and attn_fwd_split_workspace_bytes: the split
+// plan of a dense launch (no split for dtypes other than bf16).
+int split_plan_of(const attn::FwdArgs& a, int dtype, int key_chunk, attn::SplitInfo* s) {
+  *s = attn::SplitInfo{};
+  if (key_chunk < 0 || (key_chunk > 0 && key_chunk % 64 != 0) || key_chunk > (1 << 30))
+    return fail(ATTN_E_SHAPE, "key_chunk=%d must be 0 (the library's choice) or a positive multiple of 64", key_chunk);
+  if (dtype != ATTN_BF16) return ATTN_OK;
+  *s = attn::plan_fwd_split(a, key_chunk);
+  if (s->chunk > 0 && (long long)a.B * a.H * s->units > 0x7FFFFFFFLL)
+    return fail(ATTN_E_SHAPE, "key_chunk=%d cuts the launch into too many workgroups", key_chunk);
+  return ATTN_OK;
+}
+
+int run_split(const attn::FwdArgs& a, int dtype, const attn::SplitInfo& sp, float* ws, void* stream) {
+  if (sp.chunk <= 0) return run(a, dtype, stream);
+  hipError_t e = attn::launch_fwd_bf16_split(a, sp, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -205,6 +225,44 @@ int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, i
              int causal, float scale, int exp2_mode, float tau) {
   return attn_fwd_ex(Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, exp2_mode, tau, ATTN_BF16, nullptr, nullptr,
                      nullptr, nullptr);
+}
+
+long long attn_fwd_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, int causal, int dtype,
+                                         int key_chunk) {
+  // validation of everything but the pointers (stand-ins that pass those checks)
+  alignas(16) static char dummy[16];
+  attn::FwdArgs a;
+  bool nothing;
+  const uint8_t* sc = reinterpret_cast<const uint8_t*>(dummy);
+  if (validate_and_fill(a, dummy, dummy, dummy, dummy, reinterpret_cast<float*>(dummy), B, H, Nq, Nk, d, causal,
+                        1.0f, ATTN_EXP2_HW, 0.0f, dtype, sc, sc, sc, &nothing) != ATTN_OK)
+    return -1;
+  if (nothing) return 0;
+  attn::SplitInfo sp;
+  if (split_plan_of(a, dtype, key_chunk, &sp) != ATTN_OK) return -1;
+  return sp.ws_bytes;
+}
+
+int attn_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int Nq, int Nk,
+                   int d, int causal, float scale, int exp2_mode, float tau, int dtype, const uint8_t* q_scale,
+                   const uint8_t* k_scale, const uint8_t* v_scale, int key_chunk, float* workspace,
+                   long long workspace_bytes, void* stream) {
+  attn::FwdArgs a;
+  bool nothing;
+  int rc = validate_and_fill(a, Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, exp2_mode, tau, dtype, q_scale,
+                             k_scale, v_scale, &nothing);
+  if (rc != ATTN_OK) return rc;
+  attn::SplitInfo sp;
+  rc = split_plan_of(a, dtype, key_chunk, &sp);
+  if (rc != ATTN_OK || nothing) return rc;
+  if (sp.chunk > 0) {
+    if (workspace_bytes < sp.ws_bytes)
+      return fail(ATTN_E_SHAPE, "workspace of %lld bytes; attn_fwd_split_workspace_bytes gives %lld", workspace_bytes,
+                  sp.ws_bytes);
+    if (!workspace) return fail(ATTN_E_NULLPTR, "this launch is split and needs a workspace");
+    if (!aligned16(workspace)) return fail(ATTN_E_ALIGN, "workspace must be 16-byte aligned");
+  }
+  return run_split(a, dtype, sp, workspace, stream);
 }
 
 int attn_fwd_stats(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int Nq, int Nk,

@@ -53,7 +53,22 @@ struct BwdArgs {
   float scale_log2;         // scale * log2(e)
 };
 
+// Key-split plan of a dense bf16 launch: each query tile's keys cut into
+// chunks of `chunk` keys run by separate workgroups and merged (chunk 0: the
+// launch is not split).
+struct SplitInfo {
+  int chunk = 0;          // keys per chunk, a multiple of 64
+  int units = 0;          // (query tile, chunk) units per (batch, head)
+  int rows = 0;           // query rows per tile
+  long long ws_bytes = 0; // float32 workspace the split launch needs
+};
+// key_chunk 0 lets the library choose (no split when the launch already fills
+// the chip or its rows are too short to cut); otherwise that chunk size.
+SplitInfo plan_fwd_split(const FwdArgs& a, int key_chunk);
+
 // Each returns hipSuccess or the launch error; none synchronises.
+// Split launch (bf16, dense): the split kernel, then the merge kernel, on `stream`.
+hipError_t launch_fwd_bf16_split(const FwdArgs& a, const SplitInfo& s, float* ws, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 // prep pass, dK/dV kernel, dQ kernel, in that order on `stream`

@@ -29,7 +29,7 @@ def _declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert names == sorted(["attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes", "attn_exp2", "attn_fwd",
-                            "attn_fwd_ex", "attn_mx_quantize",
+                            "attn_fwd_ex", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_mx_quantize",
                             "attn_fwd_stats", "attn_fwd_varlen",
                             "attn_fwd_varlen_ex", "attn_last_error", "attn_mix_sixteenths",
                             "attn_mx_scale_offsets", "attn_mx_scale_scatter"])
@@ -121,6 +121,66 @@ def test_stats_validation(lib):
     args = [a["Q"], a["K"], a["V"], a["O"], a["LSE"], 1, 1, 128, 128, 128, 0, 0.1, 0, 8.0, 1, None, None, None]
     assert lib.attn_fwd_stats(*args, None, None) == -1
     assert lib.attn_fwd_stats(*args, FAKE + 4, None) == -8
+
+
+def _split_ws(lib, B=2, H=8, Nq=1024, Nk=1024, d=128, causal=1, dtype=1, key_chunk=0):
+    return lib.attn_fwd_split_workspace_bytes(B, H, Nq, Nk, d, causal, dtype, key_chunk)
+
+
+def _split_units(n_qt, BM, Nq, Nk, chunk, causal, diag=0):
+    """Units of a split launch per head, counted the way the planner
+    describes them: query tile qt needs the keys below its end (causal) or
+    all Nk, cut into ceil(keys / chunk) chunks, at least one."""
+    units = 0
+    for qt in range(n_qt):
+        kend = min(Nk, (qt + 1) * BM + diag) if causal else Nk
+        units += max(1, -(-kend // chunk)) if kend > 0 else 1
+    return units
+
+
+def test_split_workspace_sizes(lib):
+    # the library splits launches that would occupy under a quarter of the
+    # 256 compute units: B2 H8 N1024 causal (128 workgroups) runs whole
+    assert _split_ws(lib) == 0
+    assert _split_ws(lib, B=1, H=2) > 0                      # 16 workgroups: split
+    assert _split_ws(lib, key_chunk=128) == 2 * 8 * _split_units(8, 128, 1024, 1024, 128, True) * 128 * 129 * 4
+    assert _split_units(8, 128, 1024, 1024, 128, True) == 36
+    # explicit chunks, non-causal, ragged
+    assert _split_ws(lib, B=1, H=2, Nq=300, Nk=333, causal=0, key_chunk=64) == 2 * 3 * 6 * 128 * 129 * 4
+    assert _split_ws(lib, B=1, H=2, Nq=300, Nk=333, causal=1, key_chunk=64) == \
+        2 * _split_units(3, 128, 300, 333, 64, True) * 128 * 129 * 4
+    # d = 64 runs 256-row tiles of 64-key blocks
+    assert _split_ws(lib, B=1, H=1, Nq=100, Nk=4096, d=64, causal=0, key_chunk=128) == 32 * 256 * 65 * 4
+    # a launch that fills the chip is not split; nor are other dtypes or empty launches
+    assert _split_ws(lib, B=4, H=16, Nq=4096, Nk=4096) == 0
+    assert _split_ws(lib, dtype=0, d=64) == 0
+    assert _split_ws(lib, B=0) == 0
+    # rows too short to cut
+    assert _split_ws(lib, B=1, H=1, Nq=64, Nk=100, causal=0) == 0
+    # decoding-like: one query row, long keys
+    assert _split_ws(lib, B=1, H=8, Nq=1, Nk=32768, causal=0) > 0
+    # invalid input
+    assert _split_ws(lib, key_chunk=100) == -1
+    assert _split_ws(lib, key_chunk=-64) == -1
+    assert _split_ws(lib, d=96) == -1
+    assert _split_ws(lib, B=-1) == -1
+
+
+def test_split_validation(lib):
+    a = GOOD
+    base = [a["Q"], a["K"], a["V"], a["O"], a["LSE"], 2, 8, 1024, 1024, 128, 1, 0.088, 0, 8.0, 1, None, None, None]
+    need = _split_ws(lib, key_chunk=128)
+    assert lib.attn_fwd_split(*base, 128, FAKE, need - 4, None) == -2       # workspace too small
+    assert lib.attn_fwd_split(*base, 128, None, need, None) == -1           # no workspace
+    assert lib.attn_fwd_split(*base, 128, FAKE + 4, need, None) == -8       # unaligned workspace
+    assert lib.attn_fwd_split(*base, 96, FAKE, 1 << 40, None) == -2         # chunk not a multiple of 64
+    assert "key_chunk" in lib.attn_last_error().decode()
+    bad = list(base)
+    bad[9] = 100
+    assert lib.attn_fwd_split(*bad, 0, FAKE, need, None) == -3
+    empty = list(base)
+    empty[5] = 0
+    assert lib.attn_fwd_split(*empty, 0, None, 0, None) == 0
 
 
 def test_mix_table(lib):
