@@ -218,6 +218,37 @@ int attn_fwd_split(const void* Q, const void* K, const void* V, void* O, float* 
                    const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
                    int key_chunk, float* workspace, long long workspace_bytes, void* stream);
 
+/* Bytes of the device scratch array attn_fwd_split_noalloc uses (64 MiB). */
+enum { ATTN_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024 };
+
+/*
+ * attn_fwd_split_noalloc -- attn_fwd_split for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. The call allocates nothing (no hipMalloc, no library
+ * routine that allocates); the split launch's workspace is a file-scope
+ * device array of ATTN_NOALLOC_SCRATCH_BYTES bytes that every device the
+ * library runs on holds from load until the process ends.
+ *
+ *   arguments     those of attn_fwd_split without the workspace
+ *   key_chunk     0: the library's choice, with the chunk doubled as often as
+ *                 needed for the partials to fit the scratch (or the launch
+ *                 run whole); > 0: a multiple of 64 whose partials must fit,
+ *                 else ATTN_E_SHAPE
+ *   stream        must belong to the current device (ATTN_E_HIP otherwise);
+ *                 the scratch address of each device is looked up once, on
+ *                 the first call made with that device current
+ * Every call on a device shares that device's scratch, which keeps the last
+ * call's contents: calls that overlap on one device (other streams, other
+ * threads) race and must be ordered by the caller. Nothing in the scratch
+ * needs to start at zero. Results equal attn_fwd_split's for the same
+ * key_chunk. Errors: those of attn_fwd_split.
+ */
+int attn_fwd_split_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                           int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                           int exp2_mode, float tau, int dtype,
+                           const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                           int key_chunk, void* stream);
+
 /*
  * attn_fwd_varlen -- a batch of sequences of different lengths, packed.
  *

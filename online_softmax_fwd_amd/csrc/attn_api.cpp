@@ -199,14 +199,42 @@ int split_plan_of(const attn::FwdArgs& a, int dtype, int key_chunk, attn::SplitI
   return ATTN_OK;
 }
 
-int run_split(const attn::FwdArgs& a, int dtype, const attn::SplitInfo& sp, float* ws, void* stream) {
+}  // namespace
+
+namespace attn {
+
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+int prepare_fwd_split(FwdArgs* a, SplitInfo* sp, bool* nothing, const void* Q, const void* K, const void* V, void* O,
+                      float* LSE, int B, int H, int Nq, int Nk, int d, int causal, float scale, int exp2_mode,
+                      float tau, int dtype, const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                      int key_chunk, long long ws_cap) {
+  int rc = validate_and_fill(*a, Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, exp2_mode, tau, dtype, q_scale,
+                             k_scale, v_scale, nothing);
+  if (rc != ATTN_OK) return rc;
+  rc = split_plan_of(*a, dtype, key_chunk, sp);
+  if (rc != ATTN_OK || *nothing || ws_cap < 0 || sp->ws_bytes <= ws_cap) return rc;
+  if (key_chunk > 0)
+    return fail(ATTN_E_SHAPE, "key_chunk=%d needs %lld bytes of workspace; the library's scratch holds %lld",
+                key_chunk, sp->ws_bytes, ws_cap);
+  // the library's chunk: grow it until the partials fit
+  for (long long ch = 2LL * sp->chunk; ch <= (1 << 30); ch *= 2) {
+    *sp = plan_fwd_split(*a, (int)ch);
+    if (sp->ws_bytes == 0) break;       // no tile is cut any more
+    if (sp->ws_bytes <= ws_cap) return ATTN_OK;
+  }
+  *sp = SplitInfo{};                     // run whole
+  return ATTN_OK;
+}
+
+int run_fwd_split(const FwdArgs& a, int dtype, const SplitInfo& sp, float* ws, void* stream) {
   if (sp.chunk <= 0) return run(a, dtype, stream);
-  hipError_t e = attn::launch_fwd_bf16_split(a, sp, ws, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_fwd_bf16_split(a, sp, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
 
-}  // namespace
+}  // namespace attn
 
 extern "C" {
 
@@ -248,21 +276,19 @@ int attn_fwd_split(const void* Q, const void* K, const void* V, void* O, float* 
                    const uint8_t* k_scale, const uint8_t* v_scale, int key_chunk, float* workspace,
                    long long workspace_bytes, void* stream) {
   attn::FwdArgs a;
-  bool nothing;
-  int rc = validate_and_fill(a, Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, exp2_mode, tau, dtype, q_scale,
-                             k_scale, v_scale, &nothing);
-  if (rc != ATTN_OK) return rc;
   attn::SplitInfo sp;
-  rc = split_plan_of(a, dtype, key_chunk, &sp);
+  bool nothing;
+  int rc = attn::prepare_fwd_split(&a, &sp, &nothing, Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, exp2_mode, tau,
+                                   dtype, q_scale, k_scale, v_scale, key_chunk, -1);
   if (rc != ATTN_OK || nothing) return rc;
-  if (sp.chunk > 0) {
+  if (sp.ws_bytes > 0) {
     if (workspace_bytes < sp.ws_bytes)
       return fail(ATTN_E_SHAPE, "workspace of %lld bytes; attn_fwd_split_workspace_bytes gives %lld", workspace_bytes,
                   sp.ws_bytes);
     if (!workspace) return fail(ATTN_E_NULLPTR, "this launch is split and needs a workspace");
     if (!aligned16(workspace)) return fail(ATTN_E_ALIGN, "workspace must be 16-byte aligned");
   }
-  return run_split(a, dtype, sp, workspace, stream);
+  return attn::run_fwd_split(a, dtype, sp, workspace, stream);
 }
 
 int attn_fwd_stats(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int Nq, int Nk,

@@ -16,6 +16,9 @@
 //     LSE = ln 2 * (L + log2 sum_k w_k).
 // Tiles whose keys fit one chunk write O and LSE directly and take no part in
 // the merge.
+#include <mutex>
+
+#include "attn.h"
 #include "attn_fwd_bf16_kernels.h"
 
 namespace attn {
@@ -214,7 +217,9 @@ SplitInfo plan_d(const FwdArgs& a, int key_chunk) {
   s.chunk = chunk;
   s.units = p.units;
   s.rows = p.BM;
-  s.ws_bytes = (long long)a.B * a.H * p.units * p.BM * (D + 1) * 4;
+  // no partials when no tile is cut into more than one chunk
+  const int n_qt = (a.Nq + p.BM - 1) / p.BM;
+  s.ws_bytes = p.units > n_qt ? (long long)a.B * a.H * p.units * p.BM * (D + 1) * 4 : 0;
   return s;
 }
 
@@ -242,3 +247,71 @@ hipError_t launch_fwd_bf16_split(const FwdArgs& a, const SplitInfo& s, float* ws
 }
 
 }  // namespace attn
+
+// ---------------------------------------------------------------------------
+// attn_fwd_split_noalloc: attn_fwd_split with its workspace taken from a
+// file-scope device array instead of the caller, for callers that cannot
+// allocate device memory (code under graph capture, tight serving loops).
+//
+// `scratch` is a host-side stand-in for the array: each device holds its own
+// copy at its own address, which hipGetSymbolAddress gives with that device
+// current. That address is looked up once per device on the first call made
+// with the device current, kept, and is what the kernels receive; the array's
+// name itself is never passed to a kernel or a copy.
+// ---------------------------------------------------------------------------
+namespace attn {
+namespace {
+
+constexpr long long kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;   // per device, held until the process ends
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+static __device__ __attribute__((aligned(256))) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device `stream` belongs to, which must be the
+// current device (the address is looked up with that device current).
+int scratch_for(void* stream, float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(ATTN_E_HIP, hipGetErrorString(e));
+  if (stream != nullptr) {
+    int sdev = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return set_error(ATTN_E_HIP, hipGetErrorString(e));
+    if (sdev != dev) return set_error(ATTN_E_HIP, "the stream belongs to another device than the current one");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return set_error(ATTN_E_HIP, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return set_error(ATTN_E_HIP, e != hipSuccess ? hipGetErrorString(e) : "no scratch address");
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" int attn_fwd_split_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                                      int Nq, int Nk, int d, int causal, float scale, int exp2_mode, float tau,
+                                      int dtype, const uint8_t* q_scale, const uint8_t* k_scale,
+                                      const uint8_t* v_scale, int key_chunk, void* stream) {
+  attn::FwdArgs a;
+  attn::SplitInfo sp;
+  bool nothing;
+  int rc = attn::prepare_fwd_split(&a, &sp, &nothing, Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, exp2_mode,
+                                   tau, dtype, q_scale, k_scale, v_scale, key_chunk, attn::kScratchBytes);
+  if (rc != ATTN_OK || nothing) return rc;
+  float* ws = nullptr;
+  if (sp.ws_bytes > 0) {
+    rc = attn::scratch_for(stream, &ws);
+    if (rc != ATTN_OK) return rc;
+  }
+  return attn::run_fwd_split(a, dtype, sp, ws, stream);
+}

@@ -66,6 +66,22 @@ struct SplitInfo {
 // the chip or its rows are too short to cut); otherwise that chunk size.
 SplitInfo plan_fwd_split(const FwdArgs& a, int key_chunk);
 
+// Validation and key-split plan of attn_fwd_split (attn_api.cpp), shared
+// with its no-allocation variant: the arguments of attn_fwd_split without the
+// workspace. ws_cap >= 0 bounds the workspace: with key_chunk 0 the library's
+// chunk is doubled until its workspace fits (or no tile is cut any more and
+// the launch runs whole); an explicit key_chunk that needs more is rejected
+// (ATTN_E_SHAPE). ws_cap < 0: no bound. Returns ATTN_OK or an error code
+// with the message set for attn_last_error; *nothing: no rows to compute.
+int prepare_fwd_split(FwdArgs* a, SplitInfo* sp, bool* nothing, const void* Q, const void* K, const void* V, void* O,
+                      float* LSE, int B, int H, int Nq, int Nk, int d, int causal, float scale, int exp2_mode,
+                      float tau, int dtype, const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                      int key_chunk, long long ws_cap);
+// Runs a prepared launch: whole (sp.chunk == 0) or split with workspace ws.
+int run_fwd_split(const FwdArgs& a, int dtype, const SplitInfo& sp, float* ws, void* stream);
+// Sets this thread's message for attn_last_error and returns code.
+int set_error(int code, const char* msg);
+
 // Each returns hipSuccess or the launch error; none synchronises.
 // Split launch (bf16, dense): the split kernel, then the merge kernel, on `stream`.
 hipError_t launch_fwd_bf16_split(const FwdArgs& a, const SplitInfo& s, float* ws, hipStream_t stream);

@@ -29,7 +29,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert names == sorted(["attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes", "attn_exp2", "attn_fwd",
-                            "attn_fwd_ex", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_mx_quantize",
+                            "attn_fwd_ex", "attn_fwd_split", "attn_fwd_split_noalloc", "attn_fwd_split_workspace_bytes",
+                            "attn_mx_quantize",
                             "attn_fwd_stats", "attn_fwd_varlen",
                             "attn_fwd_varlen_ex", "attn_last_error", "attn_mix_sixteenths",
                             "attn_mx_scale_offsets", "attn_mx_scale_scatter"])
@@ -181,6 +182,26 @@ def test_split_validation(lib):
     empty = list(base)
     empty[5] = 0
     assert lib.attn_fwd_split(*empty, 0, None, 0, None) == 0
+
+
+def test_split_noalloc_validation(lib):
+    """attn_fwd_split_noalloc checks everything attn_fwd_split checks, and an
+    explicit chunk whose partials exceed its 64 MiB scratch, before it
+    touches a device."""
+    import ctypes
+    fn = lib.attn_fwd_split_noalloc
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fn.argtypes = [vp] * 5 + [ci] * 6 + [cf, ci, cf, ci, vp, vp, vp, ci, vp]
+    a = GOOD
+    ptrs = [a["Q"], a["K"], a["V"], a["O"], a["LSE"]]
+    # B=1 H=64 Nq=128 Nk=16384 cut into 64-key chunks: 64 * 256 partial slots of 128 x 129 floats
+    assert _split_ws(lib, B=1, H=64, Nq=128, Nk=16384, causal=0, key_chunk=64) == 64 * 256 * 128 * 129 * 4
+    assert fn(*ptrs, 1, 64, 128, 16384, 128, 0, 0.088, 0, 8.0, 1, None, None, None, 64, None) == -2
+    assert "scratch" in lib.attn_last_error().decode()
+    assert fn(*ptrs, 1, 64, 128, 16384, 128, 0, 0.088, 0, 8.0, 1, None, None, None, 96, None) == -2
+    assert fn(*ptrs, 1, 64, 128, 16384, 100, 0, 0.088, 0, 8.0, 1, None, None, None, 0, None) == -3
+    assert fn(None, None, None, None, None, 1, 64, 0, 16384, 128, 0, 0.088, 0, 8.0, 1, None, None, None, 0,
+              None) == 0
 
 
 def test_mix_table(lib):
