@@ -229,6 +229,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   floatx16 s[KB];        // S^T of the current tile, then its float32 P
   bf16x8 pb[KB][2];      // that P as bf16, the next MFMA phase's PV B operand
   float alpha_p = 1.0f;  // rescale factor of the tile whose P is in s
+  const float p_max = exp2_hw(tau);  // largest P the lagging max lets a row keep
   float m_run = kNegInf;  // running max, raw score units
   float l_run = 0.0f;     // running denominator over this lane's half of the keys
   unsigned long long cnt[4] = {0, 0, 0, 0};
@@ -284,6 +285,45 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           const int key = k0 + kb * 32 + 16 * (e >> 3) + 8 * hh + (e & 7);
           if (key >= Nk || (CAUSAL && key > qi + diag)) s[kb][e] = kNegInf;
         }
+    }
+    if constexpr (D == 128) {
+      // The common case without the row maximum: P from the stale maximum.
+      // Each P of a lane is at most that lane's partial row sum, so if every
+      // lane's sum is at most 2^tau, no score of this tile exceeds its row's
+      // maximum by more than tau and the rule keeps the stale maximum
+      // (factor 1) -- the decision the general path below takes, on the same
+      // P and the same sum, without its maximum trees. A row's first tile
+      // (m = -inf gives an infinite or NaN sum), a row whose maximum grew by
+      // more than tau, and counting launches take the general path on the
+      // kept scores. At d = 192 the kernel has no registers for the second
+      // copy of the scores.
+      if (j > 0 && !stats) {
+        const float mc = m_run * c;
+        floatx16 p[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) p[kb][e] = exp2_sel<EMU16>(__builtin_fmaf(s[kb][e], c, -mc), e);
+        const float ps = tree_sum<KB>(p);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!__builtin_amdgcn_ballot_w64(!(ps <= p_max))) {
+          alpha_p = 1.0f;
+          l_run = l_run + ps;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) pb[kb][cc][e] = (__bf16)p[kb][8 * cc + e];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) asm volatile("" : "+v"(pb[kb][cc]));
+          asm volatile("" : "+v"(l_run));
+          return;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     const float mx = pl_max_halves(tree_max<KB>(s));
 
