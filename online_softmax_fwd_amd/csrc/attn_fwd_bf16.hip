@@ -296,8 +296,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       // (m = -inf gives an infinite or NaN sum), a row whose maximum grew by
       // more than tau, and counting launches take the general path on the
       // kept scores. At d = 192 the kernel has no registers for the second
-      // copy of the scores.
-      if (j > 0 && !stats) {
+      // copy of the scores. Only with the hardware exp2: with the stale
+      // maximum an exponent may exceed 127, where the software exp2 wraps
+      // around instead of saturating to +inf or NaN as v_exp_f32 does.
+      if (EMU16 == 0 && j > 0 && !stats) {
         const float mc = m_run * c;
         floatx16 p[KB];
 #pragma unroll

@@ -241,6 +241,7 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = floatx16{};
   float m_run = kNegInf, l_run = 0.0f;
+  const float p_max = exp2_hw(tau);  // largest P the lagging max lets a row keep
   unsigned long long cnt[4] = {0, 0, 0, 0};
 
   auto load_tile = [&](int t, char* kd, char* vd) __attribute__((always_inline)) {
@@ -252,10 +253,28 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
     }
   };
 
-  auto compute = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
+  // O^T += V^T P^T for the tile whose P (bf16) is in pb
+  auto pv = [&](const bf16x8 (&pb)[KB][2], const char* vs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const char* vp = vs + voff[db % VP] + (db / VP) * 64 * VP + (kb * 32 + 16 * cc) * C::RB;
+          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp));
+          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp + 4 * C::RB));
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][cc], o[db], 0, 0, 0);
+        }
+  };
+
+  // S^T of tile t from the K tile at ks, masked where the tile crosses the
+  // causal diagonal or the end of the keys
+  auto scores = [&](int t, const char* ks, floatx16 (&s)[KB]) __attribute__((always_inline)) {
     const int k0 = t * BN;
-    if (CAUSAL && k0 > qw0 + 31 + diag) return;  // wave-uniform: every key of the tile is masked
-    floatx16 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -272,6 +291,49 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
           const int key = k0 + kb * 32 + 16 * (e >> 3) + 8 * hh + (e & 7);
           if (key >= Nk || (CAUSAL && key > qi + diag)) s[kb][e] = kNegInf;
         }
+    }
+  };
+
+  auto compute = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
+    const int k0 = t * BN;
+    if (CAUSAL && k0 > qw0 + 31 + diag) return;  // wave-uniform: every key of the tile is masked
+    floatx16 s[KB];
+    scores(t, ks, s);
+    bf16x8 pb[KB][2];
+    // The common case first, without the row maximum (as in the ping-pong
+    // kernel): P from the stale maximum, in place of the scores; if every
+    // lane's partial row sum is at most 2^tau, no score exceeded its row's
+    // maximum by more than tau and the lagging-max rule keeps it (factor 1).
+    // Otherwise -- a row's first tile, a grown maximum -- the scores are
+    // computed again from the K tile, which stays in LDS until the end of
+    // this step, and the general path below runs on them. Counting launches
+    // always take the general path, and so do the software-exp2 instances:
+    // with the stale maximum an exponent may exceed 127, where the software
+    // exp2 wraps around instead of saturating (the hardware one gives +inf or
+    // NaN, which the check rejects). Only at d = 128 and 192: at d = 64 and
+    // 256 the second path pushes the kernel past its register budget
+    // (spills; measured 13 % and 15 % slower).
+    if (EMU16 == 0 && (D == 128 || D == 192) && !stats) {
+      const float mc = m_run * c;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = exp2_sel<EMU16>(__builtin_fmaf(s[kb][e], c, -mc), e);
+      const float ps = tree_sum<KB>(s);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!__builtin_amdgcn_ballot_w64(!(ps <= p_max))) {
+        l_run = l_run + ps;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[kb][cc][e] = (__bf16)s[kb][8 * cc + e];
+        pv(pb, vs);
+        return;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      scores(t, ks, s);
     }
     const float mx = pl_max_halves(tree_max<KB>(s));
     const float m_new = vmax(m_run, mx);
@@ -299,27 +361,13 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = exp2_sel<EMU16>(__builtin_fmaf(s[kb][e], c, -mc), e);
     l_run = __builtin_fmaf(l_run, alpha, tree_sum<KB>(s));
-    bf16x8 pb[KB][2];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[kb][cc][e] = (__bf16)s[kb][8 * cc + e];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const char* vp = vs + voff[db % VP] + (db / VP) * 64 * VP + (kb * 32 + 16 * cc) * C::RB;
-          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp));
-          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp + 4 * C::RB));
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][cc], o[db], 0, 0, 0);
-        }
+    pv(pb, vs);
   };
 
   // double-buffered: tile t+1 is in flight while tile t is computed; each
