@@ -422,19 +422,35 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     load_tiles(0, kslot(S - 1), vslot(S - 2));
     block_sync();
   }
+  // Causal: group 0 holds the workgroup's first 128 rows, which see no key of
+  // its last tiles (up to two of them). Group 0 runs the full steps only up
+  // to the last tile one of its rows can see (Tw), PV of that tile in step
+  // Tw, and in the steps after it only its share of the tile DMAs and the
+  // barriers. The skipped tiles are fully masked for these rows (P = 0), so
+  // the result is the same.
+  int Tw = T;
+  if (CAUSAL && group == 0) Tw = max(1, min(T, (q0 + 127 + diag) / BN + 1));
   step(0, N{}, Y{}, I0{});
   int j = 1;
-  for (; j + S - 1 < T; j += S)
+  for (; j + S - 1 < Tw; j += S)
     static_for<0, S>([&](auto R) __attribute__((always_inline)) {
       step(j + R, Y{}, Y{}, std::integral_constant<int, (decltype(R)::value + 1) % S>{});
     });
-  // the remaining steps j .. T-1 (fewer than S; j = 1 mod S), then step T: PV of the last tile
+  // the remaining steps j .. Tw-1 (fewer than S; j = 1 mod S), then step Tw: PV of the last tile
   static_for<0, S - 1>([&](auto R) __attribute__((always_inline)) {
-    if (j + R < T) step(j + R, Y{}, Y{}, std::integral_constant<int, (decltype(R)::value + 1) % S>{});
+    if (j + R < Tw) step(j + R, Y{}, Y{}, std::integral_constant<int, (decltype(R)::value + 1) % S>{});
   });
   static_for<0, S>([&](auto R) __attribute__((always_inline)) {
-    if (T % S == R) step(T, Y{}, N{}, R);
+    if (Tw % S == R) step(Tw, Y{}, N{}, R);
   });
+  if (CAUSAL) {
+    for (int i = Tw + 1; i <= T; ++i) {  // group 0 only: DMA share and barriers of step i
+      load_tiles(i, kslot(i % S - 1), vslot(i % S - 2));
+      block_sync();
+      wait_batch(i);
+      block_sync();
+    }
+  }
   if (group == 0) block_sync();
 
   // ---- epilogue: O / l, LSE -------------------------------------------------
