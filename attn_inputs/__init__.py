@@ -64,6 +64,10 @@ WORKLOADS = {
         # causal d = 192 is one of them), at the headline batch and length
         Workload("bf16_b4h16_n4096_d192", 4, 16, 4096, 4096, 192, "bf16", (False, True), "mix", 8.0, 1006),
         Workload("bf16_b4h16_n4096_d256", 4, 16, 4096, 4096, 256, "bf16", (False, True), "mix", 8.0, 1007),
+        # one query row per head against a long key sequence (a decoding
+        # step): too few query tiles to fill the GPU whole, the shape the
+        # key-split launch is for
+        Workload("bf16_b1h8_nq1_nk32768_d128", 1, 8, 1, 32768, 128, "bf16", (False,), "hw", 8.0, 1008),
     ]
 }
 

@@ -14,9 +14,13 @@ Prints ONE JSON line. Besides the contract fields it carries
   roofline      for the dominant kernel (the non-causal launch): algorithmic
                 FLOPs per launch / its mean duration from HIP events recorded
                 on the launch stream inside the timed region, against the
-                dense bf16 MFMA peak of MI355X (2.5 PFLOP/s); "traffic" is the
-                calibrated HBM byte count per launch from rocprofv3 counters
-                (null when no counter run covers these kernel sources)
+                dense MFMA peak of MI355X for the dtype (bf16 2.5 PFLOP/s);
+                a launch below the ridge point (a decoding step: about one
+                FLOP per byte) reports algorithmic HBM bytes (Q, K, V read
+                once, O and LSE written once) per second against 8 TB/s
+                instead; "traffic" is the calibrated HBM byte count per launch
+                from rocprofv3 counters (null when no counter run covers these
+                kernel sources)
   rescale       lagging-max rescale counts per mode, from one counting launch
                 (attn_fwd_stats) outside the timed region
   backward      bf16 workloads at d 64 and 128 and the MXFP8 workload: the backward pass (attn_bwd) on the same
@@ -41,21 +45,23 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}   # MI355X dense MFMA, published
+PEAK_HBM_GBS = 8000.0                                              # MI355X HBM3E, published
 MODE_CODES = {"hw": 0, "emu": 1, "mix": 2}
 DEFAULT_WORKLOAD = "bf16_b4h16_n4096_d128"
 # HBM traffic of one non-causal launch of the default workload, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch, --calib-copy-mib 256). Calibrated on a plain 256 MiB device copy in
-# the same runs: FETCH_SIZE read 131088.4 KiB for 262144 KiB moved (x2.0),
+# the same runs: FETCH_SIZE read 131088 KiB for 262144 KiB moved (x2.0),
 # WRITE_SIZE read 262144 KiB (x1.0). Valid only for the kernel sources it was
 # taken on (first 16 hex digits of their SHA-256); any edit turns it off.
 TRAFFIC = {
     "workload": "bf16_b4h16_n4096_d128",
-    "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "96c0c6c7d420defa",
+    "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "bb5a0425ef3b8d42",
+                "online_softmax_fwd_amd/csrc/attn_fwd_bf16_kernels.h": "cc78a5b4f538be51",
                 "online_softmax_fwd_amd/csrc/attn_device.h": "0505e9cf734434e7",
                 "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "1249699229bb3642"},
-    "fetch_kib_raw": 98443.1, "fetch_scale": 2.0,
-    "write_kib_raw": 66560.0, "write_scale": 1.0,
+    "fetch_kib_raw": 98453.0, "fetch_scale": 2.0,
+    "write_kib_raw": 66560.7, "write_scale": 1.0,
 }
 
 
@@ -86,6 +92,9 @@ def parse():
     p.add_argument("--no-split", action="store_true",
                    help="run every launch whole (attn_fwd_ex) instead of letting the library cut small launches "
                         "into key chunks (attn_fwd_split)")
+    p.add_argument("--key-chunk", type=int, default=0,
+                   help="cut every bf16 launch into key chunks of this many keys (a multiple of 64; 0: the "
+                        "library's choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bwd", action="store_true", help="skip the backward-pass section")
     p.add_argument("--bwd-steps", type=int, default=50)
@@ -93,6 +102,17 @@ def parse():
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (HBM counter calibration)")
     return p.parse_args()
+
+
+def algorithmic_bytes(w) -> int:
+    """HBM bytes one launch must move at the least: Q, K, V read once, O and
+    LSE written once (MXFP8: one E8M0 scale byte per 32 elements of Q, K, V)."""
+    e = {"bf16": 2, "f32": 4, "mxfp8": 1}[w.dtype]
+    inp = (w.Nq + 2 * w.Nk) * w.d * e
+    if w.dtype == "mxfp8":
+        inp += (w.Nq + 2 * w.Nk) * w.d // 32
+    out = w.Nq * w.d * (4 if w.dtype == "f32" else 2) + w.Nq * 4
+    return w.B * w.H * (inp + out)
 
 
 def metric_of(w) -> str:
@@ -149,7 +169,7 @@ def cpu_baseline(w, causal_modes, flop_budget=1.2e12):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{what}, Nq=Nk={w.Nq} d={w.d}, causal modes {list(causal_modes)}; float64 numpy one-shot "
+        "sample": f"{what}, {f'Nq=Nk={w.Nq}' if w.Nq == w.Nk else f'Nq={w.Nq} Nk={w.Nk}'} d={w.d}, causal modes {list(causal_modes)}; float64 numpy one-shot "
                   f"softmax (it forms the full S even when causal; FLOPs counted as for the GPU); {dt:.1f} s on "
                   f"{threads} BLAS threads of {len(os.sched_getaffinity(0))} usable cores, {cpu_model()}",
         "cpu_model": cpu_model(),
@@ -256,7 +276,8 @@ def main():
     # runs a launch whole, as it does for launches that fill the chip)
     ws = {}
     for c in w.causal:
-        n = 0 if args.no_split else attn.split_workspace_bytes(q, k, causal=c, fp8_p=args.fp8_p)
+        n = 0 if args.no_split else attn.split_workspace_bytes(q, k, causal=c, key_chunk=args.key_chunk,
+                                                               fp8_p=args.fp8_p)
         ws[c] = torch.empty(-(-n // 4), dtype=torch.float32, device=dev) if n > 0 else None
 
     def launch(causal):
@@ -265,7 +286,7 @@ def main():
             attn.fwd(q, k, v, causal=causal, exp2_mode=mode, tau=tau, out=o, lse=l, stream=stream, **scales, **fp8)
         else:
             attn.fwd_split(q, k, v, causal=causal, exp2_mode=mode, tau=tau, out=o, lse=l, stream=stream,
-                           workspace=ws[causal], **scales, **fp8)
+                           key_chunk=args.key_chunk, workspace=ws[causal], **scales, **fp8)
 
     for _ in range(args.warmup):
         for c in w.causal:
@@ -309,6 +330,19 @@ def main():
         "pct_of_peak": round(100.0 * flops_of(w, c) / (float(np.mean(per[c])) * 1e-3) / 1e12 / peak, 2),
     } for c in w.causal}
 
+    # The bound: matrix core when the launch's FLOPs per algorithmic byte
+    # exceed the ridge point (peak FLOP/s / peak HBM B/s), else HBM.
+    kname = f"{fwd_kernel_name(w, dom, ws[dom] is not None)} (d={w.d}, {'causal' if dom else 'non-causal'})"
+    abytes = algorithmic_bytes(w)
+    if flops_of(w, dom) / abytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    else:
+        gbs = abytes / (dom_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": abytes}
+    roofline.update({"traffic": traffic_bytes(w), "traffic_unit": "bytes per launch (HBM read + write)"})
+
     mix16 = None
     if mode == "mix":
         dcode = {"f32": 0, "bf16": 1, "mxfp8": 2}[w.dtype]
@@ -338,17 +372,7 @@ def main():
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
         "per_mode": per_mode,
-        "roofline": {
-            "bound": "mfma",
-            "kernel": f"{fwd_kernel_name(w, dom, ws[dom] is not None)} (d={w.d}, "
-                      f"{'causal' if dom else 'non-causal'})",
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": traffic_bytes(w),
-            "traffic_unit": "bytes per launch (HBM read + write)",
-        },
+        "roofline": roofline,
     }
     # lagging-max rescales, one extra launch per mode outside the timed region
     rescale = {}

@@ -32,12 +32,16 @@ namespace {
 // CU instead of three, so 576 workgroups needed a second round.
 template <int D>
 using SplitCfg = StreamCfg<D>;
-// One thread per float4 of a slot (the split kernel's lane order): thread f
+// CS threads per float4 of a slot (the split kernel's lane order): float4 f
 // of a tile's slots holds row 32 * (f / 64 / (D/8)) + (f % 64) % 32 and four
-// columns of it; 256 threads per workgroup, BM * D / 1024 workgroups per
+// columns of it; 256 threads per workgroup, BM * D * CS / 1024 workgroups per
 // query tile: workgroup b handles piece b % pieces of tile qt of head bh,
-// b / pieces = bh * n_qt + qt.
-template <int D>
+// b / pieces = bh * n_qt + qt. With CS > 1 (rows cut into more chunks than
+// one thread folds in one round of loads, e.g. a decoding step) the CS
+// adjacent lanes of a float4 fold every CS-th chunk each, and their states
+// combine by the same rule across lanes, so the loads of a row's chunks are
+// in flight together instead of one group after another.
+template <int D, int CS>
 __global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __restrict__ ws, __bf16* __restrict__ O,
                                                               float* __restrict__ LSE, SplitPlan plan, int n_slots,
                                                               int n_qt, int pieces) {
@@ -47,7 +51,8 @@ __global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __res
   const int qt = bq % n_qt, bh = bq / n_qt;
   const int n = plan.n_chunks(qt);
   if (n <= 1) return;  // written by the split kernel itself
-  const int f = piece * 256 + threadIdx.x;
+  const int f = piece * (256 / CS) + threadIdx.x / CS;
+  const int c0 = threadIdx.x % CS;  // this lane's chunks: c0, c0 + CS, ...
   const int lane = f & 63, i = (f >> 6) % (D / 8), wave = (f >> 6) / (D / 8);
   const int r = 32 * wave + (lane & 31);
   const int row = qt * plan.BM + r;
@@ -60,19 +65,22 @@ __global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __res
   const float* lse2 = ws + (size_t)n_slots * plan.BM * D + slot0 * plan.BM + r;
   const floatx4* src = (const floatx4*)ws + slot0 * slot_f4 + f;
   __bf16* op = O + ((size_t)bh * plan.Nq + row) * D + col;
-  const bool lse_writer = i == 0 && lane < 32;
+  const bool lse_writer = i == 0 && lane < 32 && c0 == 0;
   // One pass with a running maximum (the same combine, applied a group of G
   // chunks at a time); group g+1 is loaded before group g is folded in, so
   // the loads of two groups are in flight at once.
   constexpr int G = 8;
   float t[2][G];
   floatx4 x[2][G];
+  // group position k0 + j is this lane's chunk c0 + CS * (k0 + j)
+  const int nl = (n - c0 + CS - 1) / CS;  // chunks of this lane (0 if c0 >= n)
   auto load = [&](int k0, int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const bool ok = k0 + j < n;
-      t[b][j] = ok ? lse2[(size_t)(k0 + j) * plan.BM] : kNegInf;
-      x[b][j] = src[(size_t)(ok ? k0 + j : k0) * slot_f4];
+      const bool ok = k0 + j < nl;
+      const size_t k = (size_t)c0 + (size_t)CS * (ok ? k0 + j : 0);
+      t[b][j] = ok ? lse2[k * plan.BM] : kNegInf;
+      x[b][j] = ok ? src[k * slot_f4] : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
   float L = kNegInf, wsum = 0.0f;
@@ -99,13 +107,31 @@ __global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __res
     }
   };
   load(0, 0);
-  for (int k0 = 0; k0 < n; k0 += 2 * G) {
-    if (k0 + G < n) load(k0 + G, 1);
+  for (int k0 = 0; k0 < nl; k0 += 2 * G) {
+    if (k0 + G < nl) load(k0 + G, 1);
     fold(0);
-    if (k0 + G >= n) break;
-    if (k0 + 2 * G < n) load(k0 + 2 * G, 0);
+    if (k0 + G >= nl) break;
+    if (k0 + 2 * G < nl) load(k0 + 2 * G, 0);
     fold(1);
   }
+  // the CS lanes of this float4 (adjacent, all past or all before the row
+  // check above) combine their states pairwise
+#pragma unroll
+  for (int off = 1; off < CS; off <<= 1) {
+    const float Lo = __shfl_xor(L, off, 64);
+    const float wo = __shfl_xor(wsum, off, 64);
+    floatx4 ao;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ao[e] = __shfl_xor(acc[e], off, 64);
+    const float Lm = fmaxf(L, Lo);
+    const float sa = L > kNegInf ? exp2_hw(L - Lm) : 0.0f;
+    const float sb = Lo > kNegInf ? exp2_hw(Lo - Lm) : 0.0f;
+    wsum = wsum * sa + wo * sb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = acc[e] * sa + ao[e] * sb;
+    L = Lm;
+  }
+  if (c0 != 0) return;
   if (!(L > kNegInf)) {  // the row saw no key in any chunk
     *(bf16x4*)op = bf16x4{};
     if (lse_writer) LSE[(size_t)bh * plan.Nq + row] = kNegInf;
@@ -185,10 +211,19 @@ hipError_t launch_split(const FwdArgs& a, const SplitInfo& s, float* ws, hipStre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qt = (a.Nq + C::BM - 1) / C::BM;
-  const int pieces = C::BM * D / 1024;
-  const long long mgrid = (long long)a.B * a.H * n_qt * pieces;
-  hipLaunchKernelGGL((fwd_split_merge_kernel<D>), dim3((unsigned)mgrid), dim3(256), 0, stream, ws, (__bf16*)a.o,
-                     a.lse, p, (int)grid, n_qt, pieces);
+  // rows of more chunks than one round of loads (8) take 8 lanes per float4
+  if (p.n_chunks(n_qt - 1) > 8) {
+    constexpr int CS = 8;
+    const int pieces = C::BM * D * CS / 1024;
+    const long long mgrid = (long long)a.B * a.H * n_qt * pieces;
+    hipLaunchKernelGGL((fwd_split_merge_kernel<D, CS>), dim3((unsigned)mgrid), dim3(256), 0, stream, ws,
+                       (__bf16*)a.o, a.lse, p, (int)grid, n_qt, pieces);
+  } else {
+    const int pieces = C::BM * D / 1024;
+    const long long mgrid = (long long)a.B * a.H * n_qt * pieces;
+    hipLaunchKernelGGL((fwd_split_merge_kernel<D, 1>), dim3((unsigned)mgrid), dim3(256), 0, stream, ws,
+                       (__bf16*)a.o, a.lse, p, (int)grid, n_qt, pieces);
+  }
   return hipGetLastError();
 }
 
