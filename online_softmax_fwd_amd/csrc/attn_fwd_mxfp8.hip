@@ -51,6 +51,10 @@ constexpr int kBM = 32 * kWaves;               // query rows per workgroup
 constexpr int kBN = 64;                        // keys per tile
 constexpr int kTile = kBN * kRB;               // bytes per K or V tile
 constexpr int kLoads = kBN * kCH / 64 / kWaves;  // wave-loads per wave per tensor per tile
+// Tiles whose K/V scale words one LDS refill holds: 2 words per tile and
+// tensor, one word per thread.
+constexpr int kScaleTiles = 64;
+static_assert(4 * kScaleTiles == kThreads, "one scale word per thread per refill");
 static_assert(kLoads * 64 * kWaves == kBN * kCH, "tile split");
 
 // Swizzle of the 16-byte chunks (position c ^ f(r)), the same for the K and
@@ -101,6 +105,10 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   __shared__ __attribute__((aligned(1024))) char kb1[kTile];
   __shared__ __attribute__((aligned(1024))) char vb0[kTile];
   __shared__ __attribute__((aligned(1024))) char vb1[kTile];
+  // E8M0 scale words of K and V (one dword = the 4 d-blocks of a 32-key
+  // block) for kScaleTiles tiles, staged in LDS (see refill_scales)
+  __shared__ uint32_t ksw[2 * kScaleTiles];
+  __shared__ uint32_t vsw[2 * kScaleTiles];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -194,17 +202,30 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
     }
   };
 
-  auto scale_word = [&](const uint8_t* base, int blk) __attribute__((always_inline)) -> uint32_t {
-    return blk < sc.kblocks ? *(const uint32_t*)(base + (size_t)blk * sc.stride) : 0x7F7F7F7Fu;
+  // The scale words of tiles t0 .. t0 + kScaleTiles - 1 into LDS, one per
+  // thread (0x7F = 2^0 past the last block). Read per tile from global
+  // memory, each word's load would be issued after the next tile's DMA and,
+  // vmcnt draining in order, waiting for it would wait for that DMA as well;
+  // a refill runs where no DMA is in flight, once per kScaleTiles tiles, and
+  // the per-tile reads become LDS reads next to the K fragment reads.
+  auto refill_scales = [&](int t0) __attribute__((always_inline)) {
+    const int w = tid % (2 * kScaleTiles);
+    const int blk = 2 * t0 + w;
+    const bool is_k = tid < 2 * kScaleTiles;
+    const uint8_t* base = (is_k ? KS : VS) + sc.kbase;
+    const uint32_t word = blk < sc.kblocks ? *(const uint32_t*)(base + (size_t)blk * sc.stride) : 0x7F7F7F7Fu;
+    if (is_k)
+      ksw[w] = word;
+    else
+      vsw[w] = word;
   };
 
   auto compute = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
     const int k0 = t * kBN;
     if ((CAUSAL && k0 > qw0 + 31 + diag) || !wave_rows) return;  // wave-uniform: nothing to add
-    const uint8_t* ksb = KS + sc.kbase;
-    const uint8_t* vsb = VS + sc.kbase;
-    const uint32_t kw0 = scale_word(ksb, 2 * t), kw1 = scale_word(ksb, 2 * t + 1);
-    const uint32_t vw0 = scale_word(vsb, 2 * t), vw1 = scale_word(vsb, 2 * t + 1);
+    const int sw = (2 * t) % (2 * kScaleTiles);
+    const uint32_t kw0 = ksw[sw], kw1 = ksw[sw + 1];
+    const uint32_t vw0 = vsw[sw], vw1 = vsw[sw + 1];
     const int kscale[2] = {(int)(kw0 >> (8 * hh)), (int)(kw1 >> (8 * hh))};
     const int vscale = (int)(hh ? vw1 : vw0);  // lane half h supplies key block 2t + h; op_sel picks d block
 
@@ -321,10 +342,15 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
     }
   };
 
+  refill_scales(0);
   load_tiles(0, kb0, vb0);
   wait_own_loads();
   __syncthreads();
   for (int t = 0; t < n_kt; t += 2) {
+    if (t > 0 && t % kScaleTiles == 0) {  // every wave is past compute(t - 1); no DMA in flight
+      refill_scales(t);
+      __syncthreads();
+    }
     if (t + 1 < n_kt) load_tiles(t + 1, kb1, vb1);
     compute(t, kb0, vb0);
     wait_own_loads();
