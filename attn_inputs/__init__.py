@@ -59,7 +59,7 @@ WORKLOADS = {
         Workload("bf16_b4h16_n4096_d128", 4, 16, 4096, 4096, 128, "bf16", (False, True), "mix", 8.0, 1003),
         Workload("bf16_b2h32_n8192_d64_causal_spiky", 2, 32, 8192, 8192, 64, "bf16", (True,), "mix", 8.0, 1004,
                  spike_frac=0.01, spike_gain=8.0),
-        Workload("mxfp8_b2h16_n8192_d128", 2, 16, 8192, 8192, 128, "mxfp8", (False,), "mix", 0.0, 1005),
+        Workload("mxfp8_b2h16_n8192_d128", 2, 16, 8192, 8192, 128, "mxfp8", (False,), "mix", 8.0, 1005),
         # the larger head dims of the tuning-table rows ("The emulated exp2":
         # causal d = 192 is one of them), at the headline batch and length
         Workload("bf16_b4h16_n4096_d192", 4, 16, 4096, 4096, 192, "bf16", (False, True), "mix", 8.0, 1006),

@@ -48,20 +48,30 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}   # MI355X dense M
 PEAK_HBM_GBS = 8000.0                                              # MI355X HBM3E, published
 MODE_CODES = {"hw": 0, "emu": 1, "mix": 2}
 DEFAULT_WORKLOAD = "bf16_b4h16_n4096_d128"
-# HBM traffic of one non-causal launch of the default workload, from two
-# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
-# dispatch, --calib-copy-mib 256). Calibrated on a plain 256 MiB device copy in
-# the same runs: FETCH_SIZE read 131088 KiB for 262144 KiB moved (x2.0),
-# WRITE_SIZE read 262144 KiB (x1.0). Valid only for the kernel sources it was
-# taken on (first 16 hex digits of their SHA-256); any edit turns it off.
+# HBM traffic of one non-causal launch, from two rocprofv3 --pmc runs of this
+# script per workload (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch,
+# --calib-copy-mib 256). Calibrated on a plain 256 MiB device copy in the
+# same runs: FETCH_SIZE read 131088 KiB for 262144 KiB moved (x2.0),
+# WRITE_SIZE read 262144 KiB (x1.0). Valid only for the kernel sources a
+# count was taken on (first 16 hex digits of their SHA-256); any edit turns
+# it off.
 TRAFFIC = {
-    "workload": "bf16_b4h16_n4096_d128",
-    "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "bb5a0425ef3b8d42",
-                "online_softmax_fwd_amd/csrc/attn_fwd_bf16_kernels.h": "cc78a5b4f538be51",
-                "online_softmax_fwd_amd/csrc/attn_device.h": "0505e9cf734434e7",
-                "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "1249699229bb3642"},
-    "fetch_kib_raw": 98453.0, "fetch_scale": 2.0,
-    "write_kib_raw": 66560.7, "write_scale": 1.0,
+    "bf16_b4h16_n4096_d128": {
+        "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "bb5a0425ef3b8d42",
+                    "online_softmax_fwd_amd/csrc/attn_fwd_bf16_kernels.h": "cc78a5b4f538be51",
+                    "online_softmax_fwd_amd/csrc/attn_device.h": "0505e9cf734434e7",
+                    "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "1249699229bb3642"},
+        "fetch_kib_raw": 98453.0, "fetch_scale": 2.0,
+        "write_kib_raw": 66560.7, "write_scale": 1.0,
+    },
+    "mxfp8_b2h16_n8192_d128": {
+        "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_mxfp8.hip": "6a054e30e9d66b2d",
+                    "online_softmax_fwd_amd/csrc/attn_mx_common.h": "3ff9393404d4e1ce",
+                    "online_softmax_fwd_amd/csrc/attn_device.h": "0505e9cf734434e7",
+                    "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "1249699229bb3642"},
+        "fetch_kib_raw": 53150.0, "fetch_scale": 2.0,
+        "write_kib_raw": 66560.0, "write_scale": 1.0,
+    },
 }
 
 
@@ -69,48 +79,24 @@ def traffic_bytes(w):
     """Calibrated HBM bytes per launch of the dominant kernel, or None when no
     counter run covers this workload and these kernel sources."""
     import hashlib
-    if w.name != TRAFFIC["workload"]:
+    t = TRAFFIC.get(w.name)
+    if t is None:
         return None
-    for rel, digest in TRAFFIC["sources"].items():
+    for rel, digest in t["sources"].items():
         with open(os.path.join(ROOT, rel), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
                 return None
-    kib = TRAFFIC["fetch_kib_raw"] * TRAFFIC["fetch_scale"] + TRAFFIC["write_kib_raw"] * TRAFFIC["write_scale"]
+    kib = t["fetch_kib_raw"] * t["fetch_scale"] + t["write_kib_raw"] * t["write_scale"]
     return int(round(kib * 1024))
-
-
-def parse():
-    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=300)
-    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    p.add_argument("--exp2-mode", default=None, help="override the workload's exp2 mode (hw, emu, mix, mixK)")
-    p.add_argument("--tau", type=float, default=None)
-    p.add_argument("--fp8-p", default="block", choices=["block", "e4m3", "e5m2"],
-                   help="MXFP8 workloads: P scaled per 32-key block, or times 2^8 with one fixed scale as E4M3 or E5M2")
-    p.add_argument("--no-split", action="store_true",
-                   help="run every launch whole (attn_fwd_ex) instead of letting the library cut small launches "
-                        "into key chunks (attn_fwd_split)")
-    p.add_argument("--key-chunk", type=int, default=0,
-                   help="cut every bf16 launch into key chunks of this many keys (a multiple of 64; 0: the "
-                        "library's choice)")
-    p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-bwd", action="store_true", help="skip the backward-pass section")
-    p.add_argument("--bwd-steps", type=int, default=50)
-    p.add_argument("--bwd-warmup", type=int, default=50)
-    p.add_argument("--calib-copy-mib", type=int, default=0,
-                   help="also run one plain device copy of this many MiB (HBM counter calibration)")
-    return p.parse_args()
 
 
 def algorithmic_bytes(w) -> int:
     """HBM bytes one launch must move at the least: Q, K, V read once, O and
-    LSE written once (MXFP8: one E8M0 scale byte per 32 elements of Q, K, V)."""
+    LSE written once (MXFP8: one E8M0 scale byte per 32x32 block of Q, K, V)."""
     e = {"bf16": 2, "f32": 4, "mxfp8": 1}[w.dtype]
     inp = (w.Nq + 2 * w.Nk) * w.d * e
     if w.dtype == "mxfp8":
-        inp += (w.Nq + 2 * w.Nk) * w.d // 32
+        inp += (w.Nq + 2 * w.Nk) * w.d // 1024
     out = w.Nq * w.d * (4 if w.dtype == "f32" else 2) + w.Nq * 4
     return w.B * w.H * (inp + out)
 
@@ -252,6 +238,8 @@ def main():
     w = WORKLOADS[args.workload]
     mode = args.exp2_mode or w.exp2_mode
     tau = w.tau if args.tau is None else args.tau
+    if w.dtype == "mxfp8" and args.fp8_p != "block" and args.tau is None:
+        tau = 0.0  # a fixed-offset P admits only tau < log2(fmt max) - 8 (0.81 for E4M3, 7.81 for E5M2)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
