@@ -101,6 +101,31 @@ def algorithmic_bytes(w) -> int:
     return w.B * w.H * (inp + out)
 
 
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=300)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--exp2-mode", default=None, help="override the workload's exp2 mode (hw, emu, mix, mixK)")
+    p.add_argument("--tau", type=float, default=None)
+    p.add_argument("--fp8-p", default="block", choices=["block", "e4m3", "e5m2"],
+                   help="MXFP8 workloads: P scaled per 32-key block, or times 2^8 with one fixed scale as E4M3 or E5M2")
+    p.add_argument("--no-split", action="store_true",
+                   help="run every launch whole (attn_fwd_ex) instead of letting the library cut small launches "
+                        "into key chunks (attn_fwd_split)")
+    p.add_argument("--key-chunk", type=int, default=0,
+                   help="cut every bf16 launch into key chunks of this many keys (a multiple of 64; 0: the "
+                        "library's choice)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-bwd", action="store_true", help="skip the backward-pass section")
+    p.add_argument("--bwd-steps", type=int, default=50)
+    p.add_argument("--bwd-warmup", type=int, default=50)
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="also run one plain device copy of this many MiB (HBM counter calibration)")
+    return p.parse_args()
+
+
 def metric_of(w) -> str:
     """The metric's name for a workload: dtype, head dim, length and the
     causal settings one step runs."""
