@@ -476,16 +476,33 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 }
 
 
-template <int D, bool CAUSAL, int EMU16, bool PACKED>
-hipError_t launch_stream(const FwdArgs& a, hipStream_t stream) {
-  constexpr int BM = StreamCfg<D>::BM;
+template <class Cf, bool CAUSAL, int EMU16, bool PACKED>
+hipError_t launch_stream_cfg(const FwdArgs& a, hipStream_t stream) {
+  constexpr int BM = Cf::BM;
   const int n_qt = (a.Nq + BM - 1) / BM;
   const long long grid = (long long)a.B * a.H * n_qt;
-  hipLaunchKernelGGL((fwd_bf16_stream_kernel<StreamCfg<D>, CAUSAL, EMU16, PACKED>), dim3((unsigned)grid), dim3(StreamCfg<D>::THREADS), 0, stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.stats, a.H,
-                     a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.bottom_right, a.cu_q, a.cu_k, a.total_q, a.total_k,
-                     SplitPlan{}, nullptr);
+  hipLaunchKernelGGL((fwd_bf16_stream_kernel<Cf, CAUSAL, EMU16, PACKED>), dim3((unsigned)grid), dim3(Cf::THREADS), 0,
+                     stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.stats,
+                     a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.bottom_right, a.cu_q, a.cu_k, a.total_q,
+                     a.total_k, SplitPlan{}, nullptr);
   return hipGetLastError();
+}
+
+// A streaming launch at d = 128 with at most one of its 128-row workgroups
+// per CU leaves the CUs it uses running one wave per SIMD, one chain of
+// dependent tiles each. There the workgroup takes 8 waves in two key parities
+// (each SIMD runs two chains over half of the keys, and the softmax of one
+// overlaps the MFMAs of the other), with the hardware exp2; counting launches
+// keep one parity, whose per-row tile sequence is the plain recurrence.
+constexpr long long kStreamParityMaxWgs = 256;
+template <int D, bool CAUSAL, int EMU16, bool PACKED>
+hipError_t launch_stream(const FwdArgs& a, hipStream_t stream) {
+  if constexpr (D == 128 && EMU16 == 0) {
+    const long long wgs = (long long)a.B * a.H * ((a.Nq + 127) / 128);
+    if (!a.stats && wgs <= kStreamParityMaxWgs)
+      return launch_stream_cfg<StreamCfgT<128, 64, 8, 2, 2>, CAUSAL, EMU16, PACKED>(a, stream);
+  }
+  return launch_stream_cfg<StreamCfg<D>, CAUSAL, EMU16, PACKED>(a, stream);
 }
 
 template <int D, bool CAUSAL, int EMU16, bool PACKED>
