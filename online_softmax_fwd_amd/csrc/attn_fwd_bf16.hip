@@ -490,17 +490,23 @@ hipError_t launch_stream_cfg(const FwdArgs& a, hipStream_t stream) {
 
 // A streaming launch at d = 128 with at most one of its 128-row workgroups
 // per CU leaves the CUs it uses running one wave per SIMD, one chain of
-// dependent tiles each. There the workgroup takes 8 waves in two key parities
-// (each SIMD runs two chains over half of the keys, and the softmax of one
-// overlaps the MFMAs of the other), with the hardware exp2; counting launches
-// keep one parity, whose per-row tile sequence is the plain recurrence.
+// dependent tiles each. There the workgroup takes 8 waves in key parities:
+// each SIMD runs two chains over a part of the keys each, and the softmax of
+// one overlaps the MFMAs of the other. With 64-row workgroups and four
+// parities when even those number at most one per CU (the launch then fills
+// every CU and a wave walks a quarter of a row's keys), else 128-row
+// workgroups and two parities. Hardware exp2 only; counting launches keep one
+// parity, whose per-row tile sequence is the plain recurrence.
 constexpr long long kStreamParityMaxWgs = 256;
 template <int D, bool CAUSAL, int EMU16, bool PACKED>
 hipError_t launch_stream(const FwdArgs& a, hipStream_t stream) {
   if constexpr (D == 128 && EMU16 == 0) {
-    const long long wgs = (long long)a.B * a.H * ((a.Nq + 127) / 128);
-    if (!a.stats && wgs <= kStreamParityMaxWgs)
-      return launch_stream_cfg<StreamCfgT<128, 64, 8, 2, 2>, CAUSAL, EMU16, PACKED>(a, stream);
+    if (!a.stats) {
+      if ((long long)a.B * a.H * ((a.Nq + 63) / 64) <= kStreamParityMaxWgs)
+        return launch_stream_cfg<StreamCfgT<128, 128, 8, 2, 4>, CAUSAL, EMU16, PACKED>(a, stream);
+      if ((long long)a.B * a.H * ((a.Nq + 127) / 128) <= kStreamParityMaxWgs)
+        return launch_stream_cfg<StreamCfgT<128, 64, 8, 2, 2>, CAUSAL, EMU16, PACKED>(a, stream);
+    }
   }
   return launch_stream_cfg<StreamCfg<D>, CAUSAL, EMU16, PACKED>(a, stream);
 }

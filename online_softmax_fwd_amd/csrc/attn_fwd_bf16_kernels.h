@@ -87,9 +87,9 @@ template <int D_, int BN_, int NW_, int WPS_, int KPAR_ = 1>
 struct StreamCfgT : Cfg<D_, BN_, NW_> {
   static constexpr int WAVES_PER_SIMD = WPS_;  // occupancy the register budget is set for
   static constexpr int STAGES = 2;             // K/V tiles of each in the LDS ring
-  // Key parities: with KPAR = 2, waves w and w + NW/2 own the same 32 rows
-  // and take the lower and the upper half of every key tile, each with its
-  // own softmax state; the two states merge exactly at the end.
+  // Key parities: waves w, w + NW/KPAR, ... own the same 32 rows and take
+  // consecutive 32-key parts of every key tile, each with its own softmax
+  // state; the states merge exactly at the end.
   static constexpr int KPAR = KPAR_;
   static constexpr int RW = NW_ / KPAR_;                      // 32-row blocks
   static constexpr int BM = 32 * RW;                          // query rows per workgroup
@@ -408,46 +408,57 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
   }
 
   if constexpr (KPAR > 1) {
-    // The second parity's state goes through LDS (the K/V ring is free after
+    // The other parities' states go through LDS (the K/V rings are free after
     // the last barrier) and the first parity's wave of the same rows merges
-    // it by the exact rule ("Combining two blocks exactly"): with M the larger
-    // maximum, each state is weighted by 2^((m - M) * c) (0 for a state that
-    // saw no key), l and O add.
-    static_assert(KPAR == 2 && C::RW % 2 == 0, "two key parities, an even number of row blocks");
-    static_assert(C::RW / 2 * (D / 8) * 64 * 16 <= S * C::TILE, "half of the second parity's O fits a ring");
-    __shared__ float xml[2 * C::RW * 64];
-    floatx4* xo = (floatx4*)(rw < C::RW / 2 ? kring : vring) + (rw % (C::RW / 2)) * (D / 8) * 64 + lane;
-    if (par == 1) {
+    // them in parity order by the exact rule ("Combining two blocks
+    // exactly"): with M the larger maximum, each state is weighted by
+    // 2^((m - M) * c) (0 for a state that saw no key), l and O add.
+    constexpr int XS = (D / 8) * 64 * 16;     // bytes of one wave's O, float4 per lane
+    constexpr int PER_RING = S * C::TILE / XS;
+    constexpr int NX = (KPAR - 1) * C::RW;    // states to exchange
+    static_assert(NX <= 2 * PER_RING, "the exchanged states fit the K and V rings");
+    __shared__ float xml[2 * NX * 64];
+    auto xslot = [&](int j) __attribute__((always_inline)) -> floatx4* {
+      return (floatx4*)(j < PER_RING ? kring + j * XS : vring + (j - PER_RING) * XS) + lane;
+    };
+    if (par > 0) {
+      const int j = (par - 1) * C::RW + rw;
+      floatx4* xo = xslot(j);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           xo[(4 * db + g) * 64] = floatx4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-      xml[rw * 64 + lane] = m_run;
-      xml[(C::RW + rw) * 64 + lane] = l_run;
+      xml[j * 64 + lane] = m_run;
+      xml[(NX + j) * 64 + lane] = l_run;
     }
     __syncthreads();
-    if (par == 1) {
+    if (par > 0) {
       if (stats && lane == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) atomicAdd(stats + i, cnt[i]);
       }
       return;
     }
-    const float m1 = xml[rw * 64 + lane], l1 = xml[(C::RW + rw) * 64 + lane];
-    const float mm = vmax(m_run, m1);
-    const float a0 = m_run > kNegInf ? exp2_hw((m_run - mm) * c) : 0.0f;
-    const float a1 = m1 > kNegInf ? exp2_hw((m1 - mm) * c) : 0.0f;
-    l_run = l_run * a0 + l1 * a1;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int p1 = 1; p1 < KPAR; ++p1) {
+      const int j = (p1 - 1) * C::RW + rw;
+      const floatx4* xo = xslot(j);
+      const float m1 = xml[j * 64 + lane], l1 = xml[(NX + j) * 64 + lane];
+      const float mm = vmax(m_run, m1);
+      const float a0 = m_run > kNegInf ? exp2_hw((m_run - mm) * c) : 0.0f;
+      const float a1 = m1 > kNegInf ? exp2_hw((m1 - mm) * c) : 0.0f;
+      l_run = l_run * a0 + l1 * a1;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const floatx4 x = xo[(4 * db + g) * 64];
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[db][4 * g + r] = o[db][4 * g + r] * a0 + x[r] * a1;
-      }
-    m_run = mm;
+        for (int g = 0; g < 4; ++g) {
+          const floatx4 x = xo[(4 * db + g) * 64];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[db][4 * g + r] = o[db][4 * g + r] * a0 + x[r] * a1;
+        }
+      m_run = mm;
+    }
   }
   const float l_tot = pl_sum_halves(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that saw no key: O = 0, LSE = -inf
