@@ -527,14 +527,21 @@ hipError_t launch_k(const FwdArgs& a, hipStream_t stream) {
 // where the streaming kernel's 128-row workgroups spread the short launch
 // wider. Measured (B4 H16 N4096, TFLOP/s, ping-pong vs streaming): d = 128
 // 1137 vs ~1050 non-causal, 1017 vs 987 causal; d = 192 1233 vs 1017 and 1078
-// vs 952; causal B2 H8 N1024 d128 31.8 vs 31.2 us. d = 64 stays on the
-// streaming kernel (faster there), d = 256 too (the ping-pong kernel's O and
-// Q operands alone take 192 of its 256 registers).
+// vs 952; causal B2 H8 N1024 d128 31.8 vs 31.2 us. Non-causal d = 128
+// launches with at most one 128-row tile per CU (hardware exp2) run the
+// streaming kernel's key parities as well. d = 64 stays on the streaming
+// kernel (faster there), d = 256 too (the ping-pong kernel's O and Q operands
+// alone take 192 of its 256 registers).
 constexpr long long kPingPongCausalMinTiles = 256;
 template <int D, bool CAUSAL, int EMU16>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   bool pingpong = D == 128 || D == 192;
   if (CAUSAL && pingpong) pingpong = (long long)a.B * a.H * ((a.Nq + 255) / 256) >= kPingPongCausalMinTiles;
+  // small non-causal d = 128 launches too: the key parities of the streaming
+  // kernel (B2 H8 N1024: 27.1 -> 17.9 us; B1 H8 N4096: 84.6 -> 76.3 us)
+  if (!CAUSAL && D == 128 && EMU16 == 0 && !a.stats &&
+      (long long)a.B * a.H * ((a.Nq + 127) / 128) <= kStreamParityMaxWgs)
+    pingpong = false;
   if constexpr (D == 128 || D == 192) {
     if (pingpong)
       return a.cu_q ? launch_k<D, CAUSAL, EMU16, true>(a, stream) : launch_k<D, CAUSAL, EMU16, false>(a, stream);

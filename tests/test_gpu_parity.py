@@ -302,11 +302,12 @@ def test_device_exp2_matches_model(attn, degree, max_rel):
 
 
 def bf16_key_tile(d, causal, B, H, Nq):
-    """Keys per tile of the bf16 kernel a launch runs (a lagging-max decision
-    is taken once per tile): the ping-pong kernel (d = 128 and 192, causal
-    only with at least 256 query tiles of 256 rows) takes 64-key tiles; the
-    streaming kernel takes 64-key tiles at d = 64 and 32-key tiles at
-    d = 128, 192 and 256."""
+    """Keys per tile of the bf16 kernel a counting launch (attn_fwd_stats)
+    runs (a lagging-max decision is taken once per tile): the ping-pong kernel
+    (d = 128 and 192, causal only with at least 256 query tiles of 256 rows)
+    takes 64-key tiles; the streaming kernel with one key parity takes 64-key
+    tiles at d = 64 and 32-key tiles at d = 128, 192 and 256. (Plain launches
+    of few tiles at d = 128 run the streaming kernel's key parities instead.)"""
     if d in (128, 192):
         pingpong = (not causal) or B * H * -(-Nq // 256) >= 256
         return 64 if pingpong else 32
@@ -361,14 +362,15 @@ def test_pingpong_rescale_parity(attn, d, causal, inputs, tau, mode):
     the rescale of O and l by alpha = 2^((m_old - m_new) * c) has to be exact
     up to rounding ("FlashAttention-4's Softmax Tricks", section "Conditional
     rescaling, and when it's exact"). The counters of the same launch must
-    show rescales. Non-causal launches are always on the ping-pong kernel;
-    causal ones take it with at least 256 query tiles of 256 rows (1 x 64
-    heads x ceil(1100 / 256) = 320)."""
+    show rescales. The shapes keep the plain launch on the ping-pong kernel
+    too: non-causal with more than 256 query tiles of 128 rows (96 heads x
+    ceil(300 / 128) = 288), causal with at least 256 of 256 rows (64 heads x
+    ceil(1100 / 256) = 320)."""
     base = "bf16_b4h16_n4096_d128" if d == 128 else "bf16_b4h16_n4096_d192"
     w = WORKLOADS[base]
     if inputs == "spiky":
         w = dataclasses.replace(w, spike_frac=0.01, spike_gain=8.0)
-    shape = dict(B=1, H=64, Nq=1100, Nk=1100) if causal else dict(B=1, H=2, Nq=300, Nk=1100)
+    shape = dict(B=1, H=64, Nq=1100, Nk=1100) if causal else dict(B=1, H=96, Nq=300, Nk=1100)
     assert bf16_key_tile(d, causal, shape["B"], shape["H"], shape["Nq"]) == 64   # the ping-pong kernel's tile
     x = make_inputs(w, **shape)
     dev = to_device(x)
@@ -383,6 +385,35 @@ def test_pingpong_rescale_parity(attn, d, causal, inputs, tau, mode):
     # the plain entry point (no counters) computes the same bits
     o2, lse2 = run_fwd(attn, dev, causal, mode, tau)
     assert np.array_equal(host64(o2), host64(o)) and np.array_equal(host64(lse2), host64(lse))
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,kpar", [(1, 2, 300, 1100, 4), (1, 16, 1024, 1024, 4), (1, 3, 1100, 300, 4),
+                                              (1, 24, 1024, 1024, 2), (2, 12, 1000, 1300, 2)])
+@pytest.mark.parametrize("inputs,tau", [("normal", 8.0), ("spiky", 0.0)])
+def test_key_parity_launches(attn, B, H, Nq, Nk, kpar, inputs, tau):
+    """Launches with few query tiles at d = 128 (hardware exp2) run the
+    streaming kernel with 4 key parities and 64-row workgroups (at most 256
+    of those) or 2 parities and 128-row workgroups (at most 256 of those):
+    waves of one row block take different keys of each tile with their own
+    softmax state, merged at the end ("Lecture 2 -- Online Softmax and
+    Numerical Correctness", section "Combining two blocks exactly"). Every
+    element against the one-shot oracle, all three causal settings, ragged
+    rows and keys, rows that see no key (bottom-right with Nq > Nk), and the
+    same bits on a second call."""
+    assert (B * H * -(-Nq // 64) <= 256) == (kpar == 4) and B * H * -(-Nq // 128) <= 256
+    w = WORKLOADS["bf16_b4h16_n4096_d128"]
+    if inputs == "spiky":
+        w = dataclasses.replace(w, spike_frac=0.01, spike_gain=8.0)
+    x = make_inputs(w, B=B, H=H, Nq=Nq, Nk=Nk)
+    dev = to_device(x)
+    for causal in (False, "top_left", "bottom_right"):
+        what = f"key parities ({kpar}) B{B} H{H} {Nq}x{Nk} causal={causal} {inputs} tau={tau}"
+        announce(what)
+        o, lse = run_fwd(attn, dev, causal, "hw", tau)
+        o_ref, lse_ref = attention_f64(x["q64"], x["k64"], x["v64"], causal=causal)
+        _compare_with_empty_rows(o, lse, o_ref, lse_ref, "bf16", what, None)
+        o2, lse2 = run_fwd(attn, dev, causal, "hw", tau)
+        assert np.array_equal(host64(o2), host64(o)) and np.array_equal(host64(lse2), host64(lse)), what
 
 
 def test_attn_fwd_null_stream_entry(attn):
