@@ -167,28 +167,45 @@ SplitPlan make_plan(const FwdArgs& a, int chunk) {
 // 12.4 us, but writing its float32 partials back from L2 at the kernel's end
 // and reading them in the merge take as long again; B=1 H=16 N=2048 (128
 // ping-pong workgroups): 64-71 us split against 54 us whole. So a launch is
-// split when it would have fewer workgroups than a quarter of the CUs, into
-// chunks of at least 128 keys sized for two workgroups per CU (measured
-// faster than three for the long rows where splitting pays: fewer chunks to
-// merge per row); no split either when the rows are too short to cut.
+// split when it would have fewer workgroups than a quarter of the CUs (or,
+// on the key-parity kernel, at most half the CUs with rows of 32 or more
+// steps), into chunks of at least 128 keys sized for two workgroups per CU
+// (measured faster than three for the long rows where splitting pays: fewer
+// chunks to merge per row); no split either when the rows are too short to
+// cut.
 constexpr int kCUs = 256;
 template <int D>
 int auto_chunk(const FwdArgs& a) {
   using C = SplitCfg<D>;
   const SplitPlan probe = make_plan<D>(a, 1 << 30);
   const int n_qt = (a.Nq + C::BM - 1) / C::BM;
-  // workgroups of the whole launch: the ping-pong kernel's 256-row tiles, or
-  // the streaming kernel's tiles (the dispatch of launch_fwd_bf16)
-  const long long pp_tiles = (long long)a.B * a.H * ((a.Nq + 255) / 256);
-  const bool pingpong = (D == 128 || D == 192) && (!a.causal || pp_tiles >= 256);
-  const long long whole_wgs = pingpong ? pp_tiles : (long long)a.B * a.H * n_qt;
-  if (whole_wgs >= kCUs / 4) return 0;
+  // workgroups of the whole launch (the dispatch of launch_fwd_bf16): at
+  // d = 128 with the hardware exp2, launches of at most 256 tiles of 128 rows
+  // run the streaming kernel's key parities (64-row tiles if there are at
+  // most 256 of those); otherwise the ping-pong kernel's 256-row tiles, or
+  // the streaming kernel's tiles
   long long keys = 0;
   int kmax = 0;
   for (int qt = 0; qt < n_qt; ++qt) {
     const int k = probe.kend(qt);
     if (k > 0) keys += k;
     kmax = k > kmax ? k : kmax;
+  }
+  const long long bh = (long long)a.B * a.H;
+  const long long pp_tiles = bh * ((a.Nq + 255) / 256);
+  if (D == 128 && a.emu16 == 0 && bh * ((a.Nq + 127) / 128) <= 256) {
+    // key parities: 4 x 32 keys per step with 64-row tiles, else 2 x 32.
+    // Measured (B = 1, 128 workgroups, non-causal, whole vs split): H4 N2048
+    // (16 steps) 25.7 vs 32.0 us, H2 N4096 (32) 45.2 vs 41.0, H1 N8192 (64)
+    // 86.9 vs 60.1; the split also wins with fewer than 64 workgroups.
+    const bool four = bh * ((a.Nq + 63) / 64) <= 256;
+    const long long wgs = four ? bh * ((a.Nq + 63) / 64) : bh * ((a.Nq + 127) / 128);
+    const int steps = (kmax + (four ? 127 : 63)) / (four ? 128 : 64);
+    if (!(wgs < kCUs / 4 || (wgs <= kCUs / 2 && steps >= 32))) return 0;
+  } else {
+    const bool pingpong = (D == 128 || D == 192) && (!a.causal || pp_tiles >= 256);
+    const long long whole_wgs = pingpong ? pp_tiles : bh * n_qt;
+    if (whole_wgs >= kCUs / 4) return 0;
   }
   keys *= (long long)a.B * a.H;
   const long long target = 2LL * kCUs;
