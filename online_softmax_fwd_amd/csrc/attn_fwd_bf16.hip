@@ -109,6 +109,11 @@ __device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&
 // of LDS) measured no faster than 2 at d = 128: the loads already arrive in
 // time.
 constexpr int kPingPongStages = 2;
+#ifndef PP_PERSIST
+#define PP_PERSIST 1
+#endif
+constexpr bool kPingPongPersist = PP_PERSIST;
+constexpr int kPingPongPersistWgs = 256;  // one per CU (8 XCDs x 32)
 
 // ---------------------------------------------------------------------------
 // Ping-pong schedule. The 8 waves form two groups of 4 (one wave of each
@@ -122,12 +127,42 @@ constexpr int kPingPongStages = 2;
 // V_j is issued at the start of half-phase 2j into the other buffer of each
 // pair and waited for at the end of half-phase 2j+1.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int EMU16, bool PACKED>
+// Persistent grid: 8 * NS workgroups, NS on each XCD (workgroup wg runs on
+// XCD wg % 8), each looping over query tiles until its share is done. XCD x
+// owns an eighth of the tiles (the batch-heads count is a multiple of 8):
+// non-causal, the contiguous logical range [x * per, (x + 1) * per) of
+// (head, tile) pairs, taken NS at a time, so that each round holds whole
+// heads whose K and V the XCD's L2 shares; causal, the heads bh = x (mod 8)
+// longest tile first (all heads' last tiles, then their second-to-last, ...),
+// dealt to the NS workgroups in alternating directions, which evens out the
+// tiles' unequal lengths (16 tiles of 8 heads on 32 workgroups: 34 key tiles
+// each). Tile k of workgroup wg, or false past its share.
+__device__ __forceinline__ bool persistent_tile(int wg, int n_wg, int k, int n_qt, int n_tiles, bool causal,
+                                                int& bh, int& qt) {
+  const int x = wg & 7, s = wg >> 3, ns = n_wg >> 3;
+  const int per = n_tiles >> 3;
+  const int p = k * ns + ((causal && (k & 1)) ? ns - 1 - s : s);
+  if (p >= per) return false;
+  if (causal) {
+    const int hpx = per / n_qt;  // heads per XCD
+    qt = n_qt - 1 - p / hpx;
+    bh = (p % hpx) * 8 + x;
+  } else {
+    const int logical = x * per + p;
+    bh = logical / n_qt;
+    qt = logical - bh * n_qt;
+  }
+  return true;
+}
+
+template <int D, bool CAUSAL, int EMU16, bool PACKED, bool PERSIST>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                      __bf16* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats,
                      int H, int Nq_dense, int Nk_dense, int n_qt, float c, float tau, int bottom_right,
-                     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
+                     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k,
+                     int n_tiles) {
+  static_assert(!(PERSIST && PACKED), "persistent launches are dense");
   using C = Cfg<D, 64, 8>;
   constexpr int BN = C::BN, KB = C::KB;
   constexpr int S = kPingPongStages;
@@ -140,14 +175,15 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int group = wave >> 2;
   const int hh = lane >> 5, l32 = lane & 31;
 
-  int bh, qt;
-  if (CAUSAL) {
-    causal_tile_of(blockIdx.x, gridDim.x, n_qt, bh, qt);
-  } else {
-    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-    bh = logical / n_qt;
-    qt = logical - bh * n_qt;
-  }
+  bf16x8 qf[D / 16];  // Q as the B operand: lane (h, n) holds Q[n][16s + 8h .. +8]
+
+  // One query tile: everything below runs per tile (returns end the tile, and
+  // are taken by the whole workgroup, so the barrier counts stay matched).
+  // pre: the previous tile already loaded this tile's Q and its first K tile;
+  // nbh >= 0: this tile loads those of tile (nbh, nqt) after its last LDS
+  // read, so that they arrive during its epilogue. Returns whether it did.
+  auto run_tile = [&](const int bh, const int qt, const bool pre, const int nbh, const int nqt)
+                      __attribute__((always_inline)) -> bool {
   const int q0 = qt * C::BM;
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + l32;
@@ -155,7 +191,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // with the row pitch a compile-time constant
   const Slice sl = slice_of(bh, H, D, Nq_dense, Nk_dense, PACKED ? cu_q : nullptr, cu_k, total_q, total_k);
   const int Nq = sl.Nq, Nk = sl.Nk;
-  if (PACKED && q0 >= Nq) return;  // a query tile past this sequence's end
+  if (PACKED && q0 >= Nq) return false;  // a query tile past this sequence's end
   const size_t qbase = sl.qbase, kbase = sl.kbase;
   const int rs = PACKED ? sl.rs : D;  // elements between rows in memory
   const int rsb = rs * 2;             // bytes between K/V rows
@@ -196,8 +232,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const u32x4 rv = raw_buffer_rsrc(V + kbase, (uint32_t)nrec);
 
   // ---- Q as the B operand: lane (h, n) holds Q[n][16s + 8h .. +8] -----------
-  bf16x8 qf[D / 16];
-  {
+  if (!pre) {
     const bool ok = qi < Nq;
     const __bf16* qp = Q + qbase + (size_t)(ok ? qi : 0) * rs + 8 * hh;
 #pragma unroll
@@ -220,7 +255,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int g = 0; g < 4; ++g) *(bf16x4*)(op + 32 * db + 8 * g) = bf16x4{};
       if (hh == 0) LSE[sl.lse + qi] = kNegInf;
     }
-    return;
+    return false;
   }
 
   floatx16 o[D / 32];
@@ -406,15 +441,18 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   using N = std::false_type;
   using I0 = std::integral_constant<int, 0>;
 
-  // prologue: K_0 .. K_{S-2} and V_0 .. V_{S-3} by every wave
+  // prologue: K_0 .. K_{S-2} and V_0 .. V_{S-3} by every wave (K_0 only with
+  // two stages, already in flight when the previous tile prefetched it)
+  if (!pre) {
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t)
+    for (int t = 0; t < S - 1; ++t)
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int slot = 1024 * (wave + 8 * i);
-      if (t < T) dma16(rk, kring + t * C::TILE + slot, kld[i] + (uint32_t)t * tile_bytes);
-      if (t < S - 2 && t < T) dma16(rv, vring + t * C::TILE + slot, vld[i] + (uint32_t)t * tile_bytes);
-    }
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int slot = 1024 * (wave + 8 * i);
+        if (t < T) dma16(rk, kring + t * C::TILE + slot, kld[i] + (uint32_t)t * tile_bytes);
+        if (t < S - 2 && t < T) dma16(rv, vring + t * C::TILE + slot, vld[i] + (uint32_t)t * tile_bytes);
+      }
+  }
   wait_own_loads();
   block_sync();
   if (group == 1) {
@@ -453,6 +491,29 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
   if (group == 0) block_sync();
 
+  // Every wave is past its last LDS read of this tile and its last use of Q:
+  // the next tile's Q and first K tile can load now, behind the epilogue.
+  bool prefetched = false;
+  if (nbh >= 0) {
+    static_assert(S == 2, "the prefetch loads the prologue of two stages: K_0");
+    const Slice sn = slice_of(nbh, H, D, Nq_dense, Nk_dense, nullptr, cu_k, total_q, total_k);
+    const int q0n = nqt * C::BM, qin = q0n + wave * 32 + l32;
+    const bool ok = qin < sn.Nq;
+    const __bf16* qp = Q + sn.qbase + (size_t)(ok ? qin : 0) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const u32x4 w = ok ? *(const u32x4*)(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+      qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+    const int kendn = CAUSAL ? min(sn.Nk, q0n + C::BM + diag) : sn.Nk;
+    if (kendn > 0) {
+      const u32x4 rkn = raw_buffer_rsrc(K + sn.kbase, (uint32_t)(sn.Nk * rsb));
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) dma16(rkn, kring + 1024 * (wave + 8 * i), kld[i]);
+    }
+    prefetched = true;
+  }
+
   // ---- epilogue: O / l, LSE -------------------------------------------------
   const float l_tot = pl_sum_halves(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that saw no key: O = 0, LSE = -inf
@@ -472,6 +533,32 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if (stats && lane == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) atomicAdd(stats + i, cnt[i]);
+  }
+  return prefetched;
+  };
+
+  if constexpr (PERSIST) {
+    int bh, qt;
+    if (!persistent_tile(blockIdx.x, gridDim.x, 0, n_qt, n_tiles, CAUSAL, bh, qt)) return;
+    bool pre = false;
+    for (int k = 0;; ++k) {
+      int nbh = -1, nqt = 0;
+      const bool more = persistent_tile(blockIdx.x, gridDim.x, k + 1, n_qt, n_tiles, CAUSAL, nbh, nqt);
+      pre = run_tile(bh, qt, pre, more ? nbh : -1, nqt);
+      if (!more) break;
+      bh = nbh;
+      qt = nqt;
+    }
+  } else {
+  int bh, qt;
+  if (CAUSAL) {
+    causal_tile_of(blockIdx.x, gridDim.x, n_qt, bh, qt);
+  } else {
+    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+    bh = logical / n_qt;
+    qt = logical - bh * n_qt;
+  }
+    run_tile(bh, qt, false, -1, 0);
   }
 }
 
@@ -515,10 +602,26 @@ template <int D, bool CAUSAL, int EMU16, bool PACKED>
 hipError_t launch_k(const FwdArgs& a, hipStream_t stream) {
   constexpr int BM = Cfg<D, 64, 8>::BM;
   const int n_qt = (a.Nq + BM - 1) / BM;  // a.Nq: the longest sequence for packed batches
-  const long long grid = (long long)a.B * a.H * n_qt;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EMU16, PACKED>), dim3((unsigned)grid), dim3(512), 0, stream,
+  const long long n_bh = (long long)a.B * a.H;
+  const long long tiles = n_bh * n_qt;
+  // Dense launches of at least two tiles per CU whose heads split evenly over
+  // the XCDs run persistent: one workgroup per CU loops over its tiles (each
+  // workgroup that ends and the next that starts on its CU cost ~2.9 us of
+  // dispatch between them, measured, next to ~100 us of work per tile).
+  // (d = 128 only: at d = 192 the loop's live state spills.)
+  if constexpr (D == 128 && !PACKED && kPingPongPersist) {
+    if (n_bh % 8 == 0 && tiles >= 2 * kPingPongPersistWgs && tiles <= 0x7FFFFFFF) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EMU16, false, true>), dim3(kPingPongPersistWgs), dim3(512), 0,
+                         stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
+                         a.stats, a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.bottom_right, a.cu_q, a.cu_k,
+                         a.total_q, a.total_k, (int)tiles);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EMU16, PACKED, false>), dim3((unsigned)tiles), dim3(512), 0, stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.stats, a.H,
-                     a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.bottom_right, a.cu_q, a.cu_k, a.total_q, a.total_k);
+                     a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.bottom_right, a.cu_q, a.cu_k, a.total_q, a.total_k,
+                     (int)tiles);
   return hipGetLastError();
 }
 
