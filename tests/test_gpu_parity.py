@@ -57,6 +57,12 @@ def _compare(o, lse, o_ref, lse_ref, dtype, what, tol_rows=None):
     err_l = np.abs(host64(lse) - lse_ref).max()
     announce(f"{what}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
     tol = TOL_O[dtype] if tol_rows is None else np.maximum(TOL_O[dtype], tol_rows + 1e-5)
+    if tol_rows is not None:
+        # how much of the derived bound the rows that need it use
+        wide = tol_rows + 1e-5 > TOL_O[dtype]
+        if wide.any():
+            announce(f"  {int(wide.sum())} rows on their derived bound: max|dO| {d_o[wide].max():.3e}, "
+                     f"largest share of the bound {(d_o[wide] / (tol_rows[wide] + 1e-5)).max():.3f}")
     assert np.isfinite(err_o) and np.all(d_o <= tol), (what, err_o)
     assert np.isfinite(err_l) and err_l <= TOL_LSE, (what, err_l)
 
@@ -577,6 +583,11 @@ def _compare_with_empty_rows(o, lse, o_ref, lse_ref, dtype, what, tol_rows=None)
     err_o = d_o[full].max() if full.any() else 0.0
     err_l = np.abs(lh[full] - lse_ref[full]).max() if full.any() else 0.0
     announce(f"{what}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} empty rows={int(empty.sum())}")
+    if tol_rows is not None:
+        wide = full & (tol_rows > TOL_O[dtype])
+        if wide.any():
+            announce(f"  {int(wide.sum())} rows on their derived bound: max|dO| {d_o[wide].max():.3e}, "
+                     f"largest share of the bound {(d_o[wide] / tol_rows[wide]).max():.3f}")
     assert np.all(np.isfinite(d_o[full])) and np.all((d_o <= tol)[full]) and err_l <= TOL_LSE, what
 
 
