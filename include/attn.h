@@ -194,11 +194,13 @@ long long attn_fwd_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, in
  *                 needs no workspace)
  *   key_chunk     0: the library's choice: a launch is split when run whole
  *                 it would occupy fewer than a quarter of the compute units
- *                 (decoding-like shapes, few heads), into chunks of at least
- *                 128 keys sized for two workgroups per compute unit; larger
- *                 launches run whole (measured: splitting gains nothing there,
- *                 the partials' memory traffic costs what the shorter chains
- *                 save);
+ *                 (decoding-like shapes, few heads), or, for d = 128 launches
+ *                 small enough for the key-parity kernel, at most half of
+ *                 them with rows of 32 or more key-tile steps; into chunks of
+ *                 at least 128 keys sized for two workgroups per compute
+ *                 unit; larger launches run whole (measured: splitting gains
+ *                 nothing there, the partials' memory traffic costs what the
+ *                 shorter chains save);
  *                 > 0: a multiple of 64, keys per chunk (bf16 launches are
  *                 then always run by the split kernels)
  *   workspace     device memory of >= attn_fwd_split_workspace_bytes(...)
