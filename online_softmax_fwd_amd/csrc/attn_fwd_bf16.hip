@@ -1,7 +1,8 @@
 // attn_fwd_bf16.hip -- bf16 attention forward for gfx950 (MI355X).
 //
-// A workgroup of 8 waves owns 256 query rows of one (batch, head); each wave
-// owns 32 rows. K and V stream through LDS in 64-key tiles, two buffers per
+// A workgroup of 8 waves owns 256 query rows of one (batch, head) (128 or 64
+// in small launches, with key parities: see below); each wave owns 32 rows.
+// K and V stream through LDS in 64-key tiles, two buffers per
 // tensor; per row the wave keeps a running max m (raw score units), a
 // denominator l and a 32 x d float accumulator, so S and P never reach
 // memory. Per tile and wave:
@@ -126,6 +127,15 @@ constexpr int kPingPongPersistWgs = 256;  // one per CU (8 XCDs x 32)
 // V_{j-1} are read in the two half-phases 2j and 2j+1; the DMA for K_{j+1} and
 // V_j is issued at the start of half-phase 2j into the other buffer of each
 // pair and waited for at the end of half-phase 2j+1.
+//
+// Key parities (KPAR = 2 or 4, small launches at d = 128): the workgroup
+// owns 256 / KPAR rows; waves w, w + 8/KPAR, ... hold the same 32 rows and
+// take consecutive 32-key parts of every tile of 32 * KPAR keys (one tile
+// holds 64 or 128 keys), each with its own m, l and O; the parities of a row
+// block split over the two groups, so the phases still alternate on every
+// SIMD. At the end the states merge exactly through LDS ("Lecture 2 --
+// Online Softmax and Numerical Correctness", section "Combining two blocks
+// exactly").
 // ---------------------------------------------------------------------------
 // Persistent grid: 8 * NS workgroups, NS on each XCD (workgroup wg runs on
 // XCD wg % 8), each looping over query tiles until its share is done. XCD x
@@ -155,7 +165,7 @@ __device__ __forceinline__ bool persistent_tile(int wg, int n_wg, int k, int n_q
   return true;
 }
 
-template <int D, bool CAUSAL, int EMU16, bool PACKED, bool PERSIST>
+template <int D, bool CAUSAL, int EMU16, bool PACKED, bool PERSIST, int KPAR = 1>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                      __bf16* __restrict__ O, float* __restrict__ LSE, unsigned long long* __restrict__ stats,
@@ -163,17 +173,28 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k,
                      int n_tiles) {
   static_assert(!(PERSIST && PACKED), "persistent launches are dense");
-  using C = Cfg<D, 64, 8>;
-  constexpr int BN = C::BN, KB = C::KB;
+  static_assert(KPAR == 1 || (D == 128 && !PERSIST && (KPAR == 2 || KPAR == 4)), "key parities");
+  // KPAR key parities: waves w, w + RW, ... own the same 32 rows and take
+  // consecutive 32-key parts of every key tile, each with its own softmax
+  // state, merged exactly at the end (one parity: 64-key tiles, 256 rows)
+  constexpr int RW = 8 / KPAR;                    // 32-row blocks per workgroup
+  constexpr int BM = 32 * RW;                     // query rows per workgroup
+  constexpr int KB = KPAR == 1 ? 2 : 1;           // 32-key blocks per wave per tile
+  using C = Cfg<D, 32 * KB * KPAR, 8>;
+  constexpr int BN = C::BN;
   constexpr int S = kPingPongStages;
   __shared__ __attribute__((aligned(1024))) char kring[S * C::TILE];
   __shared__ __attribute__((aligned(1024))) char vring[S * C::TILE];
+  constexpr int NX = (KPAR - 1) * RW;  // softmax states the other parities hand over at the end
+  __shared__ float xml[NX > 0 ? 2 * NX * 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = wave >> 2;
   const int hh = lane >> 5, l32 = lane & 31;
+  const int rw = wave % RW, par = wave / RW;  // row block, key parity
+  const int kw = par * KB * 32;               // first key of this wave's part of a tile
 
   bf16x8 qf[D / 16];  // Q as the B operand: lane (h, n) holds Q[n][16s + 8h .. +8]
 
@@ -184,8 +205,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // read, so that they arrive during its epilogue. Returns whether it did.
   auto run_tile = [&](const int bh, const int qt, const bool pre, const int nbh, const int nqt)
                       __attribute__((always_inline)) -> bool {
-  const int q0 = qt * C::BM;
-  const int qw0 = q0 + wave * 32;
+  const int q0 = qt * BM;
+  const int qw0 = q0 + rw * 32;
   const int qi = qw0 + l32;
   // PACKED: a sequence of a packed batch (rows H*D apart); else dense [B,H,N,D]
   // with the row pitch a compile-time constant
@@ -210,13 +231,13 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   {
     const int krow = key_of_row(l32);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) koff[s] = kr + krow * C::RB + 16 * ((2 * s + hh) ^ swz_k<D>(krow));
+    for (int s = 0; s < D / 16; ++s) koff[s] = kr + (kw + krow) * C::RB + 16 * ((2 * s + hh) ^ swz_k<D>(krow));
     const int L = lane & 15, gidx = (lane >> 4) & 1;
     const int vr = 8 * hh + (L >> 2);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int cch = 4 * db + 2 * gidx + ((L & 3) >> 1);
-      voff[db] = vbase + vr * C::RB + 16 * (cch ^ swz_v<D>(vr)) + 8 * (L & 1);
+      voff[db] = vbase + (kw + vr) * C::RB + 16 * (cch ^ swz_v<D>(vr)) + 8 * (L & 1);
     }
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
@@ -244,10 +265,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // causal: key j is hidden from query i when j > i + diag (diag = 0 aligns the
   // mask top-left, Nk - Nq bottom-right)
-  const int kend = CAUSAL ? min(Nk, q0 + C::BM + diag) : Nk;
+  const int kend = CAUSAL ? min(Nk, q0 + BM + diag) : Nk;
   const int T = (kend + BN - 1) / BN;
   if (T <= 0) {  // no row of this workgroup sees a key (bottom-right, Nq > Nk)
-    if (qi < Nq) {
+    if (par == 0 && qi < Nq) {
       __bf16* op = O + qbase + (size_t)qi * rs + 4 * hh;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -311,8 +332,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // VALU phase j: softmax of tile j
   auto valu_phase = [&](int j) __attribute__((always_inline)) {
-    const int k0 = j * BN;
-    if ((CAUSAL && k0 + BN - 1 > qw0 + diag) || (k0 + BN > Nk)) {
+    const int k0 = j * BN + kw;  // first key of this wave's part of tile j
+    if ((CAUSAL && k0 + KB * 32 - 1 > qw0 + diag) || (k0 + KB * 32 > Nk)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -467,7 +488,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // barriers. The skipped tiles are fully masked for these rows (P = 0), so
   // the result is the same.
   int Tw = T;
-  if (CAUSAL && group == 0) Tw = max(1, min(T, (q0 + 127 + diag) / BN + 1));
+  if (CAUSAL && KPAR == 1 && group == 0) Tw = max(1, min(T, (q0 + 127 + diag) / BN + 1));
   step(0, N{}, Y{}, I0{});
   int j = 1;
   for (; j + S - 1 < Tw; j += S)
@@ -497,7 +518,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if (nbh >= 0) {
     static_assert(S == 2, "the prefetch loads the prologue of two stages: K_0");
     const Slice sn = slice_of(nbh, H, D, Nq_dense, Nk_dense, nullptr, cu_k, total_q, total_k);
-    const int q0n = nqt * C::BM, qin = q0n + wave * 32 + l32;
+    const int q0n = nqt * BM, qin = q0n + rw * 32 + l32;
     const bool ok = qin < sn.Nq;
     const __bf16* qp = Q + sn.qbase + (size_t)(ok ? qin : 0) * D + 8 * hh;
 #pragma unroll
@@ -505,13 +526,65 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       const u32x4 w = ok ? *(const u32x4*)(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
       qf[s] = __builtin_bit_cast(bf16x8, w);
     }
-    const int kendn = CAUSAL ? min(sn.Nk, q0n + C::BM + diag) : sn.Nk;
+    const int kendn = CAUSAL ? min(sn.Nk, q0n + BM + diag) : sn.Nk;
     if (kendn > 0) {
       const u32x4 rkn = raw_buffer_rsrc(K + sn.kbase, (uint32_t)(sn.Nk * rsb));
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) dma16(rkn, kring + 1024 * (wave + 8 * i), kld[i]);
     }
     prefetched = true;
+  }
+
+  if constexpr (KPAR > 1) {
+    // The other parities' states go through LDS (the K/V rings are free after
+    // the last barrier) and the first parity's wave of the same rows merges
+    // them in parity order by the exact rule ("Combining two blocks
+    // exactly"): with M the larger maximum, each state is weighted by
+    // 2^((m - M) * c) (0 for a state that saw no key), l and O add.
+    constexpr int XS = (D / 8) * 64 * 16;  // bytes of one wave's O, float4 per lane
+    constexpr int PER_RING = S * C::TILE / XS;
+    static_assert(NX <= 2 * PER_RING, "the exchanged states fit the K and V rings");
+    auto xslot = [&](int j) __attribute__((always_inline)) -> floatx4* {
+      return (floatx4*)(j < PER_RING ? kring + j * XS : vring + (j - PER_RING) * XS) + lane;
+    };
+    if (par > 0) {
+      const int j = (par - 1) * RW + rw;
+      floatx4* xo = xslot(j);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          xo[(4 * db + g) * 64] = floatx4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+      xml[j * 64 + lane] = m_run;
+      xml[(NX + j) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (par > 0) {
+      if (stats && lane == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) atomicAdd(stats + i, cnt[i]);
+      }
+      return false;
+    }
+#pragma unroll
+    for (int p1 = 1; p1 < KPAR; ++p1) {
+      const int j = (p1 - 1) * RW + rw;
+      const floatx4* xo = xslot(j);
+      const float m1 = xml[j * 64 + lane], l1 = xml[(NX + j) * 64 + lane];
+      const float mm = vmax(m_run, m1);
+      const float a0 = m_run > kNegInf ? exp2_hw((m_run - mm) * c) : 0.0f;
+      const float a1 = m1 > kNegInf ? exp2_hw((m1 - mm) * c) : 0.0f;
+      l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const floatx4 x = xo[(4 * db + g) * 64];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[db][4 * g + r] = o[db][4 * g + r] * a0 + x[r] * a1;
+        }
+      m_run = mm;
+    }
   }
 
   // ---- epilogue: O / l, LSE -------------------------------------------------
@@ -575,26 +648,30 @@ hipError_t launch_stream_cfg(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// A streaming launch at d = 128 with at most one of its 128-row workgroups
-// per CU leaves the CUs it uses running one wave per SIMD, one chain of
-// dependent tiles each. There the workgroup takes 8 waves in key parities:
-// each SIMD runs two chains over a part of the keys each, and the softmax of
-// one overlaps the MFMAs of the other. With 64-row workgroups and four
-// parities when even those number at most one per CU (the launch then fills
-// every CU and a wave walks a quarter of a row's keys), else 128-row
-// workgroups and two parities. Hardware exp2 only; counting launches keep one
-// parity, whose per-row tile sequence is the plain recurrence.
-constexpr long long kStreamParityMaxWgs = 256;
+// A d = 128 launch with at most one 128-row workgroup per CU leaves the CUs
+// it uses with little work each. There the ping-pong kernel takes key
+// parities: waves w and w + RW own the same rows and split every key tile, so
+// a workgroup covers fewer rows and its chain of tiles is shorter, and the
+// two groups still alternate MFMA and softmax phases on every SIMD. With
+// 64-row workgroups and four parities when even those number at most one per
+// CU (the launch then fills every CU and a wave walks a quarter of a row's
+// keys), else 128-row workgroups and two parities. Hardware exp2 only;
+// counting launches keep one parity, whose per-row tile sequence is the plain
+// recurrence.
+constexpr long long kParityMaxWgs = 256;
+template <bool CAUSAL, int EMU16, bool PACKED, int KPAR>
+hipError_t launch_parity(const FwdArgs& a, hipStream_t stream) {
+  constexpr int BM = 256 / KPAR;
+  const int n_qt = (a.Nq + BM - 1) / BM;  // a.Nq: the longest sequence for packed batches
+  const long long tiles = (long long)a.B * a.H * n_qt;
+  hipLaunchKernelGGL((fwd_bf16_kernel<128, CAUSAL, EMU16, PACKED, false, KPAR>), dim3((unsigned)tiles), dim3(512), 0,
+                     stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.stats,
+                     a.H, a.Nq, a.Nk, n_qt, a.scale_log2, a.tau, a.bottom_right, a.cu_q, a.cu_k, a.total_q, a.total_k,
+                     (int)tiles);
+  return hipGetLastError();
+}
 template <int D, bool CAUSAL, int EMU16, bool PACKED>
 hipError_t launch_stream(const FwdArgs& a, hipStream_t stream) {
-  if constexpr (D == 128 && EMU16 == 0) {
-    if (!a.stats) {
-      if ((long long)a.B * a.H * ((a.Nq + 63) / 64) <= kStreamParityMaxWgs)
-        return launch_stream_cfg<StreamCfgT<128, 128, 8, 2, 4>, CAUSAL, EMU16, PACKED>(a, stream);
-      if ((long long)a.B * a.H * ((a.Nq + 127) / 128) <= kStreamParityMaxWgs)
-        return launch_stream_cfg<StreamCfgT<128, 64, 8, 2, 2>, CAUSAL, EMU16, PACKED>(a, stream);
-    }
-  }
   return launch_stream_cfg<StreamCfg<D>, CAUSAL, EMU16, PACKED>(a, stream);
 }
 
@@ -630,21 +707,27 @@ hipError_t launch_k(const FwdArgs& a, hipStream_t stream) {
 // where the streaming kernel's 128-row workgroups spread the short launch
 // wider. Measured (B4 H16 N4096, TFLOP/s, ping-pong vs streaming): d = 128
 // 1137 vs ~1050 non-causal, 1017 vs 987 causal; d = 192 1233 vs 1017 and 1078
-// vs 952; causal B2 H8 N1024 d128 31.8 vs 31.2 us. Non-causal d = 128
-// launches with at most one 128-row tile per CU (hardware exp2) run the
-// streaming kernel's key parities as well. d = 64 stays on the streaming
-// kernel (faster there), d = 256 too (the ping-pong kernel's O and Q operands
-// alone take 192 of its 256 registers).
+// vs 952; causal B2 H8 N1024 d128 31.8 vs 31.2 us. Small d = 128 launches
+// (hardware exp2, not counting) run the ping-pong kernel's key parities
+// instead, causal or not. d = 64 stays on the streaming kernel (faster
+// there), d = 256 too (the ping-pong kernel's O and Q operands alone take 192
+// of its 256 registers).
 constexpr long long kPingPongCausalMinTiles = 256;
 template <int D, bool CAUSAL, int EMU16>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+  if constexpr (D == 128 && EMU16 == 0) {
+    if (!a.stats) {
+      const long long bh = (long long)a.B * a.H;
+      if (bh * ((a.Nq + 63) / 64) <= kParityMaxWgs)
+        return a.cu_q ? launch_parity<CAUSAL, EMU16, true, 4>(a, stream)
+                      : launch_parity<CAUSAL, EMU16, false, 4>(a, stream);
+      if (bh * ((a.Nq + 127) / 128) <= kParityMaxWgs)
+        return a.cu_q ? launch_parity<CAUSAL, EMU16, true, 2>(a, stream)
+                      : launch_parity<CAUSAL, EMU16, false, 2>(a, stream);
+    }
+  }
   bool pingpong = D == 128 || D == 192;
   if (CAUSAL && pingpong) pingpong = (long long)a.B * a.H * ((a.Nq + 255) / 256) >= kPingPongCausalMinTiles;
-  // small non-causal d = 128 launches too: the key parities of the streaming
-  // kernel (B2 H8 N1024: 27.1 -> 17.9 us; B1 H8 N4096: 84.6 -> 76.3 us)
-  if (!CAUSAL && D == 128 && EMU16 == 0 && !a.stats &&
-      (long long)a.B * a.H * ((a.Nq + 127) / 128) <= kStreamParityMaxWgs)
-    pingpong = false;
   if constexpr (D == 128 || D == 192) {
     if (pingpong)
       return a.cu_q ? launch_k<D, CAUSAL, EMU16, true>(a, stream) : launch_k<D, CAUSAL, EMU16, false>(a, stream);

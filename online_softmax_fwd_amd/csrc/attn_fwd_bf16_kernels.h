@@ -83,18 +83,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 // d = 192, 256: 4 waves x 32-key tiles, two workgroups per CU (the O
 // accumulators alone take d/2 VGPRs, Q another d/4; 48 / 64 KB of LDS each);
 // d = 192 only for small causal launches.
-template <int D_, int BN_, int NW_, int WPS_, int KPAR_ = 1>
+template <int D_, int BN_, int NW_, int WPS_>
 struct StreamCfgT : Cfg<D_, BN_, NW_> {
   static constexpr int WAVES_PER_SIMD = WPS_;  // occupancy the register budget is set for
   static constexpr int STAGES = 2;             // K/V tiles of each in the LDS ring
-  // Key parities: waves w, w + NW/KPAR, ... own the same 32 rows and take
-  // consecutive 32-key parts of every key tile, each with its own softmax
-  // state; the states merge exactly at the end.
-  static constexpr int KPAR = KPAR_;
-  static constexpr int RW = NW_ / KPAR_;                      // 32-row blocks
-  static constexpr int BM = 32 * RW;                          // query rows per workgroup
-  static constexpr int KBW = Cfg<D_, BN_, NW_>::KB / KPAR_;   // 32-key blocks per wave per tile
-  static_assert(RW * KPAR_ == NW_ && KBW * KPAR_ == Cfg<D_, BN_, NW_>::KB, "parity split");
 };
 template <int D>
 using StreamCfg = StreamCfgT<D, D == 64 ? 64 : 32, D == 64 ? 8 : 4, D == 64 ? 4 : D == 128 ? 3 : 2>;
@@ -156,10 +148,8 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
                             const int* __restrict__ cu_k, int total_q, int total_k, SplitPlan plan,
                             float* __restrict__ ws) {
   constexpr int D = C::D, BN = C::BN, NW = C::NW, S = C::STAGES;
-  constexpr int KB = C::KBW;  // 32-key blocks a wave takes of each tile
-  constexpr int KPAR = C::KPAR;
+  constexpr int KB = C::KB;  // 32-key blocks per tile
   static_assert(!(SPLIT && PACKED), "key splitting is for dense batches");
-  static_assert(!(SPLIT && KPAR > 1), "one key parity in split launches");
   __shared__ __attribute__((aligned(1024))) char kring[S * C::TILE];
   __shared__ __attribute__((aligned(1024))) char vring[S * C::TILE];
 
@@ -167,9 +157,6 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, l32 = lane & 31;
-  const int rw = KPAR == 1 ? wave : wave % C::RW;  // this wave's 32-row block
-  const int par = KPAR == 1 ? 0 : wave / C::RW;     // and key parity
-  const int kw = par * KB * 32;         // its first key within a tile
 
   int bh, qt;
   int unit = 0, chunk = 0, unit0 = 0, n_ch = 1;  // SPLIT: this workgroup's unit and chunk
@@ -189,7 +176,7 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
     qt = logical - bh * n_qt;
   }
   const int q0 = qt * C::BM;
-  const int qw0 = q0 + rw * 32;
+  const int qw0 = q0 + wave * 32;
   const int qi = qw0 + l32;
   const Slice sl = slice_of(bh, H, D, Nq_dense, Nk_dense, PACKED ? cu_q : nullptr, cu_k, total_q, total_k);
   const int Nq = sl.Nq, Nk = sl.Nk;
@@ -275,7 +262,7 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const char* vp = vs + voff[db % VP] + (db / VP) * 64 * VP + (kw + kb * 32 + 16 * cc) * C::RB;
+          const char* vp = vs + voff[db % VP] + (db / VP) * 64 * VP + (kb * 32 + 16 * cc) * C::RB;
           const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp));
           const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp + 4 * C::RB));
           const bf16x8 a = __builtin_bit_cast(
@@ -293,16 +280,16 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 a = *(const bf16x8*)(ks + (kw + kb * 32) * C::RB + koff[st % KP] + (st / KP) * 32 * KP);
+        const bf16x8 a = *(const bf16x8*)(ks + kb * 32 * C::RB + koff[st % KP] + (st / KP) * 32 * KP);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? floatx16{} : s[kb], 0, 0, 0);
       }
     }
-    if ((CAUSAL && k0 + kw + KB * 32 - 1 > qw0 + diag) || (k0 + kw + KB * 32 > Nk)) {
+    if ((CAUSAL && k0 + BN - 1 > qw0 + diag) || (k0 + BN > Nk)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kw + kb * 32 + 16 * (e >> 3) + 8 * hh + (e & 7);
+          const int key = k0 + kb * 32 + 16 * (e >> 3) + 8 * hh + (e & 7);
           if (key >= Nk || (CAUSAL && key > qi + diag)) s[kb][e] = kNegInf;
         }
     }
@@ -310,7 +297,7 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
 
   auto compute = [&](int t, const char* ks, const char* vs) __attribute__((always_inline)) {
     const int k0 = t * BN;
-    if (CAUSAL && k0 + kw > qw0 + 31 + diag) return;  // wave-uniform: every key of its share is masked
+    if (CAUSAL && k0 > qw0 + 31 + diag) return;  // wave-uniform: every key of the tile is masked
     floatx16 s[KB];
     scores(t, ks, s);
     bf16x8 pb[KB][2];
@@ -407,59 +394,6 @@ void fwd_bf16_stream_kernel(const __bf16* __restrict__ Q, const __bf16* __restri
     __syncthreads();
   }
 
-  if constexpr (KPAR > 1) {
-    // The other parities' states go through LDS (the K/V rings are free after
-    // the last barrier) and the first parity's wave of the same rows merges
-    // them in parity order by the exact rule ("Combining two blocks
-    // exactly"): with M the larger maximum, each state is weighted by
-    // 2^((m - M) * c) (0 for a state that saw no key), l and O add.
-    constexpr int XS = (D / 8) * 64 * 16;     // bytes of one wave's O, float4 per lane
-    constexpr int PER_RING = S * C::TILE / XS;
-    constexpr int NX = (KPAR - 1) * C::RW;    // states to exchange
-    static_assert(NX <= 2 * PER_RING, "the exchanged states fit the K and V rings");
-    __shared__ float xml[2 * NX * 64];
-    auto xslot = [&](int j) __attribute__((always_inline)) -> floatx4* {
-      return (floatx4*)(j < PER_RING ? kring + j * XS : vring + (j - PER_RING) * XS) + lane;
-    };
-    if (par > 0) {
-      const int j = (par - 1) * C::RW + rw;
-      floatx4* xo = xslot(j);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          xo[(4 * db + g) * 64] = floatx4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-      xml[j * 64 + lane] = m_run;
-      xml[(NX + j) * 64 + lane] = l_run;
-    }
-    __syncthreads();
-    if (par > 0) {
-      if (stats && lane == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(stats + i, cnt[i]);
-      }
-      return;
-    }
-#pragma unroll
-    for (int p1 = 1; p1 < KPAR; ++p1) {
-      const int j = (p1 - 1) * C::RW + rw;
-      const floatx4* xo = xslot(j);
-      const float m1 = xml[j * 64 + lane], l1 = xml[(NX + j) * 64 + lane];
-      const float mm = vmax(m_run, m1);
-      const float a0 = m_run > kNegInf ? exp2_hw((m_run - mm) * c) : 0.0f;
-      const float a1 = m1 > kNegInf ? exp2_hw((m1 - mm) * c) : 0.0f;
-      l_run = l_run * a0 + l1 * a1;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const floatx4 x = xo[(4 * db + g) * 64];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[db][4 * g + r] = o[db][4 * g + r] * a0 + x[r] * a1;
-        }
-      m_run = mm;
-    }
-  }
   const float l_tot = pl_sum_halves(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that saw no key: O = 0, LSE = -inf
   if (SPLIT && n_ch > 1) {

@@ -181,9 +181,9 @@ int auto_chunk(const FwdArgs& a) {
   const int n_qt = (a.Nq + C::BM - 1) / C::BM;
   // workgroups of the whole launch (the dispatch of launch_fwd_bf16): at
   // d = 128 with the hardware exp2, launches of at most 256 tiles of 128 rows
-  // run the streaming kernel's key parities (64-row tiles if there are at
-  // most 256 of those); otherwise the ping-pong kernel's 256-row tiles, or
-  // the streaming kernel's tiles
+  // run the ping-pong kernel's key parities (64-row tiles if there are at
+  // most 256 of those); otherwise its 256-row tiles, or the streaming
+  // kernel's tiles
   long long keys = 0;
   int kmax = 0;
   for (int qt = 0; qt < n_qt; ++qt) {

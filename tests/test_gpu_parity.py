@@ -313,7 +313,7 @@ def bf16_key_tile(d, causal, B, H, Nq):
     (d = 128 and 192, causal only with at least 256 query tiles of 256 rows)
     takes 64-key tiles; the streaming kernel with one key parity takes 64-key
     tiles at d = 64 and 32-key tiles at d = 128, 192 and 256. (Plain launches
-    of few tiles at d = 128 run the streaming kernel's key parities instead.)"""
+    of few tiles at d = 128 run the ping-pong kernel's key parities instead.)"""
     if d in (128, 192):
         pingpong = (not causal) or B * H * -(-Nq // 256) >= 256
         return 64 if pingpong else 32
@@ -398,7 +398,7 @@ def test_pingpong_rescale_parity(attn, d, causal, inputs, tau, mode):
 @pytest.mark.parametrize("inputs,tau", [("normal", 8.0), ("spiky", 0.0)])
 def test_key_parity_launches(attn, B, H, Nq, Nk, kpar, inputs, tau):
     """Launches with few query tiles at d = 128 (hardware exp2) run the
-    streaming kernel with 4 key parities and 64-row workgroups (at most 256
+    ping-pong kernel with 4 key parities and 64-row workgroups (at most 256
     of those) or 2 parities and 128-row workgroups (at most 256 of those):
     waves of one row block take different keys of each tile with their own
     softmax state, merged at the end ("Lecture 2 -- Online Softmax and
