@@ -185,8 +185,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   constexpr int S = kPingPongStages;
   __shared__ __attribute__((aligned(1024))) char kring[S * C::TILE];
   __shared__ __attribute__((aligned(1024))) char vring[S * C::TILE];
-  constexpr int NX = (KPAR - 1) * RW;  // softmax states the other parities hand over at the end
-  __shared__ float xml[NX > 0 ? 2 * NX * 64 : 1];
+  __shared__ float xml[KPAR > 1 ? 2 * 8 * 64 : 1];  // key parities: every wave's m and l at the end
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -536,55 +535,91 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 
   if constexpr (KPAR > 1) {
-    // The other parities' states go through LDS (the K/V rings are free after
-    // the last barrier) and the first parity's wave of the same rows merges
-    // them in parity order by the exact rule ("Combining two blocks
-    // exactly"): with M the larger maximum, each state is weighted by
-    // 2^((m - M) * c) (0 for a state that saw no key), l and O add.
-    constexpr int XS = (D / 8) * 64 * 16;  // bytes of one wave's O, float4 per lane
-    constexpr int PER_RING = S * C::TILE / XS;
-    static_assert(NX <= 2 * PER_RING, "the exchanged states fit the K and V rings");
-    auto xslot = [&](int j) __attribute__((always_inline)) -> floatx4* {
-      return (floatx4*)(j < PER_RING ? kring + j * XS : vring + (j - PER_RING) * XS) + lane;
+    // The parities' states merge by the exact rule ("Combining two blocks
+    // exactly"): with M the largest maximum of a row, each state is weighted
+    // by 2^((m - M) * c) (0 for a state that saw no key), l and O add. Every
+    // wave merges and stores its own slice of the columns (BPP 32-column
+    // blocks, parity q the blocks q * BPP ..), so the work spreads over all
+    // waves: each writes the blocks it does not keep into the free K/V rings
+    // (4 KiB per block, float4 per lane) and its m and l into xml, and after
+    // one barrier reads its blocks of the other parities of its rows.
+    constexpr int BPP = (D / 32) / KPAR;      // 32-column blocks a parity keeps
+    constexpr int NB = D / 32 - BPP;          // blocks a wave hands over
+    constexpr int XB = 64 * 16 * 4;           // bytes of one block
+    constexpr int RING = S * C::TILE;
+    static_assert(8 * NB * XB <= 2 * RING && RING % XB == 0, "the handed-over blocks fit the K and V rings");
+    auto xblock = [&](int w, int db) __attribute__((always_inline)) -> floatx4* {
+      const int pw = w / RW;  // the parity of wave w
+      const int k = db < pw * BPP ? db : db - BPP;
+      const int off = (w * NB + k) * XB;
+      return (floatx4*)(off < RING ? kring + off : vring + (off - RING)) + lane;
     };
-    if (par > 0) {
-      const int j = (par - 1) * RW + rw;
-      floatx4* xo = xslot(j);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db) {
+      if (db / BPP == par) continue;
+      floatx4* xo = xblock(wave, db);
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          xo[(4 * db + g) * 64] = floatx4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-      xml[j * 64 + lane] = m_run;
-      xml[(NX + j) * 64 + lane] = l_run;
+      for (int g = 0; g < 4; ++g) xo[g * 64] = floatx4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
     }
+    xml[wave * 64 + lane] = m_run;
+    xml[(8 + wave) * 64 + lane] = l_run;
     __syncthreads();
-    if (par > 0) {
-      if (stats && lane == 0) {
+    float mp[KPAR], lp[KPAR];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(stats + i, cnt[i]);
-      }
-      return false;
+    for (int p1 = 0; p1 < KPAR; ++p1) {
+      mp[p1] = xml[(p1 * RW + rw) * 64 + lane];
+      lp[p1] = xml[(8 + p1 * RW + rw) * 64 + lane];
     }
+    float mm = mp[0];
 #pragma unroll
-    for (int p1 = 1; p1 < KPAR; ++p1) {
-      const int j = (p1 - 1) * RW + rw;
-      const floatx4* xo = xslot(j);
-      const float m1 = xml[j * 64 + lane], l1 = xml[(NX + j) * 64 + lane];
-      const float mm = vmax(m_run, m1);
-      const float a0 = m_run > kNegInf ? exp2_hw((m_run - mm) * c) : 0.0f;
-      const float a1 = m1 > kNegInf ? exp2_hw((m1 - mm) * c) : 0.0f;
-      l_run = l_run * a0 + l1 * a1;
+    for (int p1 = 1; p1 < KPAR; ++p1) mm = vmax(mm, mp[p1]);
+    float a[KPAR];
+    float lsum = 0.0f;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int p1 = 0; p1 < KPAR; ++p1) {
+      a[p1] = mp[p1] > kNegInf ? exp2_hw((mp[p1] - mm) * c) : 0.0f;
+      lsum = __builtin_fmaf(lp[p1], a[p1], lsum);
+    }
+    const float l_tot = pl_sum_halves(lsum);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that saw no key: O = 0, LSE = -inf
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      if (db / BPP != par) continue;  // wave-uniform; db stays a constant index into o
+      floatx16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int p1 = 0; p1 < KPAR; ++p1) {
+        if (p1 == par) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(o[db][e], a[p1], acc[e]);
+        } else {
+          const floatx4* xo = xblock(p1 * RW + rw, db);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const floatx4 x = xo[g * 64];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[4 * g + r] = __builtin_fmaf(x[r], a[p1], acc[4 * g + r]);
+          }
+        }
+      }
+      if (qi < Nq) {
+        __bf16* op = O + qbase + (size_t)qi * rs + 4 * hh + 32 * db;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const floatx4 x = xo[(4 * db + g) * 64];
+          bf16x4 w;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[db][4 * g + r] = o[db][4 * g + r] * a0 + x[r] * a1;
+          for (int r = 0; r < 4; ++r) w[r] = (__bf16)(acc[4 * g + r] * inv);
+          *(bf16x4*)(op + 8 * g) = w;
         }
-      m_run = mm;
+      }
     }
+    if (par == 0 && qi < Nq && hh == 0) LSE[sl.lse + qi] = (mm * c + __builtin_log2f(l_tot)) * 0.693147180559945309f;
+    if (stats && lane == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atomicAdd(stats + i, cnt[i]);
+    }
+    return prefetched;
   }
 
   // ---- epilogue: O / l, LSE -------------------------------------------------
