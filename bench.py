@@ -57,12 +57,12 @@ DEFAULT_WORKLOAD = "bf16_b4h16_n4096_d128"
 # it off.
 TRAFFIC = {
     "bf16_b4h16_n4096_d128": {
-        "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "bb5a0425ef3b8d42",
-                    "online_softmax_fwd_amd/csrc/attn_fwd_bf16_kernels.h": "cc78a5b4f538be51",
+        "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "16d5c806bf7d3fc4",
+                    "online_softmax_fwd_amd/csrc/attn_fwd_bf16_kernels.h": "03acac41df8458b1",
                     "online_softmax_fwd_amd/csrc/attn_device.h": "0505e9cf734434e7",
                     "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "1249699229bb3642"},
-        "fetch_kib_raw": 98453.0, "fetch_scale": 2.0,
-        "write_kib_raw": 66560.7, "write_scale": 1.0,
+        "fetch_kib_raw": 98463.5, "fetch_scale": 2.0,
+        "write_kib_raw": 66560.0, "write_scale": 1.0,
     },
     "mxfp8_b2h16_n8192_d128": {
         "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_mxfp8.hip": "6a054e30e9d66b2d",
@@ -188,15 +188,24 @@ def cpu_baseline(w, causal_modes, flop_budget=1.2e12):
     }
 
 
-def fwd_kernel_name(w, causal: bool, split: bool = False) -> str:
+def fwd_kernel_name(w, causal: bool, split: bool = False, hw_exp2: bool = True) -> str:
     """The kernel a launch of this workload runs (the bf16 path has a
     ping-pong kernel for d = 128 and 192, causal only with at least 256 query
-    tiles of 256 rows, and a streaming kernel for everything else; a split
-    launch runs the streaming kernel over key chunks, then a merge kernel)."""
+    tiles of 256 rows, at d = 128 with hardware exp2 also for launches of at
+    most 256 workgroups of 128 rows, with key parities; and a streaming kernel
+    for everything else; a split launch runs the streaming kernel over key
+    chunks, then a merge kernel). hw_exp2: the launch computes every
+    exponential in hardware (exp2 mode "hw", or "mix" at 0 sixteenths)."""
     if split:
         return "fwd_bf16_stream_kernel (key chunks) + fwd_split_merge_kernel"
     if w.dtype == "bf16":
-        pingpong = w.d in (128, 192) and ((not causal) or w.B * w.H * -(-w.Nq // 256) >= 256)
+        bh = w.B * w.H
+        if w.d == 128 and hw_exp2:
+            if bh * -(-w.Nq // 64) <= 256:
+                return "fwd_bf16_kernel (4 key parities)"
+            if bh * -(-w.Nq // 128) <= 256:
+                return "fwd_bf16_kernel (2 key parities)"
+        pingpong = w.d in (128, 192) and ((not causal) or bh * -(-w.Nq // 256) >= 256)
         return "fwd_bf16_kernel" if pingpong else "fwd_bf16_stream_kernel"
     return f"fwd_{w.dtype}_kernel"
 
@@ -343,9 +352,16 @@ def main():
         "pct_of_peak": round(100.0 * flops_of(w, c) / (float(np.mean(per[c])) * 1e-3) / 1e12 / peak, 2),
     } for c in w.causal}
 
+    mix16 = None
+    if mode == "mix":
+        dcode = {"f32": 0, "bf16": 1, "mxfp8": 2}[w.dtype]
+        mix16 = {("causal" if c else "noncausal"): lib.attn_mix_sixteenths(dcode, w.d, int(c)) for c in w.causal}
+    hw_exp2 = mode == "hw" or (mode == "mix" and mix16["causal" if dom else "noncausal"] == 0)
+
     # The bound: matrix core when the launch's FLOPs per algorithmic byte
     # exceed the ridge point (peak FLOP/s / peak HBM B/s), else HBM.
-    kname = f"{fwd_kernel_name(w, dom, ws[dom] is not None)} (d={w.d}, {'causal' if dom else 'non-causal'})"
+    kname = (f"{fwd_kernel_name(w, dom, ws[dom] is not None, hw_exp2)} "
+             f"(d={w.d}, {'causal' if dom else 'non-causal'})")
     abytes = algorithmic_bytes(w)
     if flops_of(w, dom) / abytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2), "peak": peak,
@@ -355,11 +371,6 @@ def main():
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": abytes}
     roofline.update({"traffic": traffic_bytes(w), "traffic_unit": "bytes per launch (HBM read + write)"})
-
-    mix16 = None
-    if mode == "mix":
-        dcode = {"f32": 0, "bf16": 1, "mxfp8": 2}[w.dtype]
-        mix16 = {("causal" if c else "noncausal"): lib.attn_mix_sixteenths(dcode, w.d, int(c)) for c in w.causal}
 
     result = {
         "metric": metric_of(w),
