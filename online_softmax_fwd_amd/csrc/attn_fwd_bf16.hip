@@ -105,6 +105,18 @@ __device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&
   }
 }
 
+// One wave-load of a tile DMA (as dma16) into LDS address lds (wave-uniform).
+__device__ __forceinline__ void dma16_at(const u32x4& rs, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(off), "s"(rs)
+               : "memory");
+}
+// The raw buffer descriptor rs moved off bytes forward: the base advances
+// (48-bit address) and the size shrinks by as much (off must not exceed it).
+__device__ __forceinline__ u32x4 advance_rsrc(const u32x4& rs, uint32_t off) {
+  const uint64_t b = (((uint64_t)(rs[1] & 0xFFFFu) << 32) | rs[0]) + off;
+  return u32x4{(uint32_t)b, ((uint32_t)(b >> 32) & 0xFFFFu) | (rs[1] & 0xFFFF0000u), rs[2] - off, rs[3]};
+}
+
 // Depth of the ping-pong kernel's K/V ring in LDS (tiles of each): a tile's
 // DMA is issued 2S - 2 half-phases before its first reader. Depth 3 (96 KiB
 // of LDS) measured no faster than 2 at d = 128: the loads already arrive in
@@ -289,16 +301,23 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   float l_run = 0.0f;     // running denominator over this lane's half of the keys
   unsigned long long cnt[4] = {0, 0, 0, 0};
 
-  // DMA batch b: this wave's share of K_{b+S-1} (into kdst) and V_{b+S-2}
-  // (into vdst), the tiles that MFMA phase b+S-1 reads
-  auto load_tiles = [&](int b, char* kdst, char* vdst) __attribute__((always_inline)) {
+  // DMA batch b: this wave's share of K_{b+S-1} (into ring slot ks) and
+  // V_{b+S-2} (into slot vs), the tiles that MFMA phase b+S-1 reads. The
+  // tile's byte offset goes into a copy of the buffer descriptor (base
+  // advanced, size shortened: scalar arithmetic, and the range check still
+  // zero-fills past the last key) rather than into every lane's offset, and
+  // M0 is the ring's LDS base plus a constant.
+  auto load_tiles = [&](int b, uint32_t ks, uint32_t vs) __attribute__((always_inline)) {
+    const int tk = b + S - 1, tv = b + S - 2;
+    if (tk < T) {
+      const u32x4 r = advance_rsrc(rk, (uint32_t)tk * tile_bytes);
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int slot = 1024 * (wave + 8 * i);
-      if (b + S - 1 < T)
-        dma16(rk, kdst + slot, kld[i] + (uint32_t)(b + S - 1) * tile_bytes);
-      if (b + S - 2 < T)
-        dma16(rv, vdst + slot, vld[i] + (uint32_t)(b + S - 2) * tile_bytes);
+      for (int i = 0; i < C::LOADS; ++i) dma16_at(r, kr + ks + 1024 * (wave + 8 * i), kld[i]);
+    }
+    if (tv < T) {
+      const u32x4 r = advance_rsrc(rv, (uint32_t)tv * tile_bytes);
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) dma16_at(r, vbase + vs + 1024 * (wave + 8 * i), vld[i]);
     }
   };
   // Wait until batch j - S + 2 (issued S - 2 batches before the newest, j)
@@ -443,16 +462,14 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // every other step runs the full MFMA phase for every wave, also on tiles
   // that the causal mask empties for some of its rows (the softmax turns those
   // into P = 0), which keeps the loop free of data-dependent branches.
-  auto kslot = [&](int i) __attribute__((always_inline)) -> char* { return kring + ((i % S + S) % S) * C::TILE; };
-  auto vslot = [&](int i) __attribute__((always_inline)) -> char* { return vring + ((i % S + S) % S) * C::TILE; };
   auto slot_off = [&](int i) __attribute__((always_inline)) -> uint32_t { return ((i % S + S) % S) * C::TILE; };
   auto step = [&](int j, auto do_pv, auto do_qk, auto slot) __attribute__((always_inline)) {
     constexpr int r = decltype(slot)::value;  // j % S
-    if (group == 0) load_tiles(j, kslot(r - 1), vslot(r - 2));
+    if (group == 0) load_tiles(j, slot_off(r - 1), slot_off(r - 2));
     mfma_phase(do_pv, do_qk, slot_off(r), slot_off(r - 1));
     if (group == 1) wait_batch(j);
     block_sync();
-    if (group == 1) load_tiles(j + 1, kslot(r), vslot(r - 1));
+    if (group == 1) load_tiles(j + 1, slot_off(r), slot_off(r - 1));
     if constexpr (decltype(do_qk)::value) valu_phase(j);
     if (group == 0) wait_batch(j);
     block_sync();
@@ -477,7 +494,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   block_sync();
   if (group == 1) {
     // group 1's share of batch 0 goes out with group 0's, at half-phase 0
-    load_tiles(0, kslot(S - 1), vslot(S - 2));
+    load_tiles(0, slot_off(S - 1), slot_off(S - 2));
     block_sync();
   }
   // Causal: group 0 holds the workgroup's first 128 rows, which see no key of
@@ -503,7 +520,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   });
   if (CAUSAL) {
     for (int i = Tw + 1; i <= T; ++i) {  // group 0 only: DMA share and barriers of step i
-      load_tiles(i, kslot(i % S - 1), vslot(i % S - 2));
+      load_tiles(i, slot_off(i % S - 1), slot_off(i % S - 2));
       block_sync();
       wait_batch(i);
       block_sync();
