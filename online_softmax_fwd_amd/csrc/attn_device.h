@@ -221,5 +221,19 @@ __device__ __forceinline__ void dma16(const u32x4& rs, const char* lds, uint32_t
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(rs)
                : "memory");
 }
+// The same with the LDS destination as a wave-uniform 32-bit LDS address.
+__device__ __forceinline__ void dma16_at(const u32x4& rs, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(off), "s"(rs)
+               : "memory");
+}
+// The raw buffer descriptor rs moved off bytes forward: the base advances
+// (48-bit address) and the size shrinks by as much (off must not exceed it).
+// A tile loop puts the tile's offset here (scalar arithmetic, once per tile)
+// instead of into every lane's offset, and the range check still returns
+// zeros past the end.
+__device__ __forceinline__ u32x4 advance_rsrc(const u32x4& rs, uint32_t off) {
+  const uint64_t b = (((uint64_t)(rs[1] & 0xFFFFu) << 32) | rs[0]) + off;
+  return u32x4{(uint32_t)b, ((uint32_t)(b >> 32) & 0xFFFFu) | (rs[1] & 0xFFFF0000u), rs[2] - off, rs[3]};
+}
 
 }  // namespace attn

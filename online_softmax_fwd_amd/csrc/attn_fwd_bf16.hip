@@ -105,18 +105,6 @@ __device__ __forceinline__ void mfma_sequence(floatx16 (&o)[D / 32], floatx16 (&
   }
 }
 
-// One wave-load of a tile DMA (as dma16) into LDS address lds (wave-uniform).
-__device__ __forceinline__ void dma16_at(const u32x4& rs, uint32_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(off), "s"(rs)
-               : "memory");
-}
-// The raw buffer descriptor rs moved off bytes forward: the base advances
-// (48-bit address) and the size shrinks by as much (off must not exceed it).
-__device__ __forceinline__ u32x4 advance_rsrc(const u32x4& rs, uint32_t off) {
-  const uint64_t b = (((uint64_t)(rs[1] & 0xFFFFu) << 32) | rs[0]) + off;
-  return u32x4{(uint32_t)b, ((uint32_t)(b >> 32) & 0xFFFFu) | (rs[1] & 0xFFFF0000u), rs[2] - off, rs[3]};
-}
-
 // Depth of the ping-pong kernel's K/V ring in LDS (tiles of each): a tile's
 // DMA is issued 2S - 2 half-phases before its first reader. Depth 3 (96 KiB
 // of LDS) measured no faster than 2 at d = 128: the loads already arrive in

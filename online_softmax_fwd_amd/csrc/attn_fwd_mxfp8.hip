@@ -194,11 +194,13 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
   unsigned long long cnt[4] = {0, 0, 0, 0};
 
   auto load_tiles = [&](int t, char* kd, char* vd) __attribute__((always_inline)) {
+    const u32x4 rkt = advance_rsrc(rk, (uint32_t)t * tile_bytes), rvt = advance_rsrc(rv, (uint32_t)t * tile_bytes);
+    const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_address(kd)), vl = __builtin_amdgcn_readfirstlane(lds_address(vd));
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int slot = 1024 * (wave + kWaves * i);
-      dma16(rk, kd + slot, kld[i] + (uint32_t)t * tile_bytes);
-      dma16(rv, vd + slot, vld[i] + (uint32_t)t * tile_bytes);
+      const uint32_t slot = 1024 * (wave + kWaves * i);
+      dma16_at(rkt, kl + slot, kld[i]);
+      dma16_at(rvt, vl + slot, vld[i]);
     }
   };
 
