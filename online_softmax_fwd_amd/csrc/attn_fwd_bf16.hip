@@ -143,14 +143,28 @@ constexpr int kPingPongPersistWgs = 256;  // one per CU (8 XCDs x 32)
 // non-causal, the contiguous logical range [x * per, (x + 1) * per) of
 // (head, tile) pairs, taken NS at a time, so that each round holds whole
 // heads whose K and V the XCD's L2 shares; causal, the heads bh = x (mod 8)
-// longest tile first (all heads' last tiles, then their second-to-last, ...),
-// dealt to the NS workgroups in alternating directions, which evens out the
-// tiles' unequal lengths (16 tiles of 8 heads on 32 workgroups: 34 key tiles
-// each). Tile k of workgroup wg, or false past its share.
+// G = NS / n_qt at a time when that divides evenly (round k: the tiles of G
+// heads, one per workgroup, longest first in even rounds and shortest first
+// in odd ones, so every workgroup's sum is the same: 34 key tiles each for
+// 16 tiles of 8 heads on 32 workgroups), else longest tile first over all
+// the XCD's heads, dealt in alternating directions. Tile k of workgroup wg,
+// or false past its share.
 __device__ __forceinline__ bool persistent_tile(int wg, int n_wg, int k, int n_qt, int n_tiles, bool causal,
                                                 int& bh, int& qt) {
   const int x = wg & 7, s = wg >> 3, ns = n_wg >> 3;
   const int per = n_tiles >> 3;
+  if (causal && ns % n_qt == 0 && (per / n_qt) % (ns / n_qt) == 0) {
+    // G = NS / n_qt heads at a time (round k: heads kG .. kG + G - 1 of the
+    // XCD, one tile per workgroup), so that few heads' K and V are in flight
+    // in the XCD's L2; the tiles' lengths alternate direction between rounds
+    // (round k even: longest first), which evens out each workgroup's sum
+    const int G = ns / n_qt, hpx = per / n_qt;
+    if (k >= hpx / G) return false;
+    const int r = s / G;
+    qt = (k & 1) ? r : n_qt - 1 - r;
+    bh = (k * G + s % G) * 8 + x;
+    return true;
+  }
   const int p = k * ns + ((causal && (k & 1)) ? ns - 1 - s : s);
   if (p >= per) return false;
   if (causal) {

@@ -422,6 +422,29 @@ def test_key_parity_launches(attn, B, H, Nq, Nk, kpar, inputs, tau):
         assert np.array_equal(host64(o2), host64(o)) and np.array_equal(host64(lse2), host64(lse)), what
 
 
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 64, 2000, 2100), (2, 32, 2048, 1900)])
+def test_persistent_pingpong_parity(attn, B, H, Nq, Nk):
+    """Dense d = 128 launches with at least 512 tiles of 256 rows whose heads
+    split evenly over the 8 XCDs run the persistent ping-pong grid (one
+    workgroup per CU looping over its tiles, the next tile's Q and first K
+    tile loaded behind the current one's epilogue; causal tiles dealt G heads
+    at a time with alternating tile lengths). Every element against the
+    one-shot oracle, all three causal settings, ragged rows and keys, and the
+    same bits on a second call."""
+    assert (B * H) % 8 == 0 and B * H * -(-Nq // 256) >= 512
+    w = WORKLOADS["bf16_b4h16_n4096_d128"]
+    x = make_inputs(w, B=B, H=H, Nq=Nq, Nk=Nk)
+    dev = to_device(x)
+    for causal in (False, "top_left", "bottom_right"):
+        what = f"persistent B{B} H{H} {Nq}x{Nk} causal={causal}"
+        announce(what)
+        o, lse = run_fwd(attn, dev, causal, "hw", 8.0)
+        o_ref, lse_ref = attention_f64(x["q64"], x["k64"], x["v64"], causal=causal)
+        _compare_with_empty_rows(o, lse, o_ref, lse_ref, "bf16", what, None)
+        o2, lse2 = run_fwd(attn, dev, causal, "hw", 8.0)
+        assert np.array_equal(host64(o2), host64(o)) and np.array_equal(host64(lse2), host64(lse)), what
+
+
 def test_attn_fwd_null_stream_entry(attn):
     """attn_fwd, the 14-argument bf16 entry point on the null stream, called
     through ctypes as a C caller would, against the oracle (non-causal and
