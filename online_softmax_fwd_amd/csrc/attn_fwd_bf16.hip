@@ -354,12 +354,15 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   auto valu_phase = [&](int j) __attribute__((always_inline)) {
     const int k0 = j * BN + kw;  // first key of this wave's part of tile j
     if ((CAUSAL && k0 + KB * 32 - 1 > qw0 + diag) || (k0 + KB * 32 > Nk)) {
+      const int lim = (CAUSAL ? min(Nk - 1, qi + diag) : Nk - 1) - (k0 + 8 * hh);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kb * 32 + 16 * (e >> 3) + 8 * hh + (e & 7);
-          if (key >= Nk || (CAUSAL && key > qi + diag)) s[kb][e] = kNegInf;
+          // key k0 + 8h + off is hidden when off > lim (past the last key or
+          // the causal diagonal): one compare with a constant per element
+          const int off = kb * 32 + 16 * (e >> 3) + (e & 7);
+          if (off > lim) s[kb][e] = kNegInf;
         }
     }
     if constexpr (D == 128) {
