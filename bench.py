@@ -57,19 +57,19 @@ DEFAULT_WORKLOAD = "bf16_b4h16_n4096_d128"
 # it off.
 TRAFFIC = {
     "bf16_b4h16_n4096_d128": {
-        "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "16d5c806bf7d3fc4",
-                    "online_softmax_fwd_amd/csrc/attn_fwd_bf16_kernels.h": "03acac41df8458b1",
-                    "online_softmax_fwd_amd/csrc/attn_device.h": "0505e9cf734434e7",
+        "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "8d0fb6013d42518e",
+                    "online_softmax_fwd_amd/csrc/attn_fwd_bf16_kernels.h": "ed434fc3a23e1aa4",
+                    "online_softmax_fwd_amd/csrc/attn_device.h": "16bf28b574555d97",
                     "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "1249699229bb3642"},
-        "fetch_kib_raw": 98463.5, "fetch_scale": 2.0,
+        "fetch_kib_raw": 98467.5, "fetch_scale": 2.0,
         "write_kib_raw": 66560.0, "write_scale": 1.0,
     },
     "mxfp8_b2h16_n8192_d128": {
-        "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_mxfp8.hip": "6a054e30e9d66b2d",
+        "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_mxfp8.hip": "280fe15064e37a4a",
                     "online_softmax_fwd_amd/csrc/attn_mx_common.h": "3ff9393404d4e1ce",
-                    "online_softmax_fwd_amd/csrc/attn_device.h": "0505e9cf734434e7",
+                    "online_softmax_fwd_amd/csrc/attn_device.h": "16bf28b574555d97",
                     "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "1249699229bb3642"},
-        "fetch_kib_raw": 53150.0, "fetch_scale": 2.0,
+        "fetch_kib_raw": 53567.2, "fetch_scale": 2.0,
         "write_kib_raw": 66560.0, "write_scale": 1.0,
     },
 }
