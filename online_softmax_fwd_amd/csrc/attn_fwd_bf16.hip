@@ -207,6 +207,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int group = wave >> 2;
   const int hh = lane >> 5, l32 = lane & 31;
   const int rw = wave % RW, par = wave / RW;  // row block, key parity
+  // a counting launch, as a scalar: tested per tile, a pointer compare kept
+  // as a lane mask cost two vector instructions a step
+  const int counting = __builtin_amdgcn_readfirstlane(stats != nullptr ? 1 : 0);
   const int kw = par * KB * 32;               // first key of this wave's part of a tile
 
   bf16x8 qf[D / 16];  // Q as the B operand: lane (h, n) holds Q[n][16s + 8h .. +8]
@@ -378,7 +381,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       // copy of the scores. Only with the hardware exp2: with the stale
       // maximum an exponent may exceed 127, where the software exp2 wraps
       // around instead of saturating to +inf or NaN as v_exp_f32 does.
-      if (EMU16 == 0 && j > 0 && !stats) {
+      if (EMU16 == 0 && j > 0 && !counting) {
         const float mc = m_run * c;
         floatx16 p[KB];
 #pragma unroll
@@ -413,7 +416,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const bool seen = mx > kNegInf;
     const bool commit = seen && !(acc >= -tau);
     alpha_p = commit ? exp2_hw(acc) : 1.0f;
-    if (stats) {
+    if (counting) {
       const bool step = seen && (m_run > kNegInf) && hh == 0 && qi < Nq;
       const unsigned long long bs = __builtin_amdgcn_ballot_w64(step);
       const unsigned long long br = __builtin_amdgcn_ballot_w64(step && commit);
