@@ -462,7 +462,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // both groups; group 1 runs it one barrier later. K_t and V_t sit in ring
   // slot t % S. DMA batch b (K_{b+S-1}, V_{b+S-2}) is issued at half-phase 2b
   // (group 0 at the start of its MFMA phase b, group 1 at the start of its
-  // VALU phase b-1), into the slots of K_{b-1} and V_{b-2}, which every wave
+  // VALU phase b-1; batch 0 by every wave in the prologue), into the slots of
+  // K_{b-1} and V_{b-2}, which every wave
   // finished reading in MFMA phase b-1, and waited for at the end of
   // half-phase 2b + 2S - 3, just before MFMA phase b+S-1 reads it. The slots
   // are compile-time constants (the loop is unrolled S times), so every LDS
@@ -473,7 +474,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   auto slot_off = [&](int i) __attribute__((always_inline)) -> uint32_t { return ((i % S + S) % S) * C::TILE; };
   auto step = [&](int j, auto do_pv, auto do_qk, auto slot) __attribute__((always_inline)) {
     constexpr int r = decltype(slot)::value;  // j % S
-    if (group == 0) load_tiles(j, slot_off(r - 1), slot_off(r - 2));
+    if (group == 0 && j > 0) load_tiles(j, slot_off(r - 1), slot_off(r - 2));  // batch 0: in the prologue
     mfma_phase(do_pv, do_qk, slot_off(r), slot_off(r - 1));
     if (group == 1) wait_batch(j);
     block_sync();
@@ -486,25 +487,19 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   using N = std::false_type;
   using I0 = std::integral_constant<int, 0>;
 
-  // prologue: K_0 .. K_{S-2} and V_0 .. V_{S-3} by every wave (K_0 only with
-  // two stages, already in flight when the previous tile prefetched it)
+  // prologue: K_0 and DMA batch 0 (K_1, V_0) by every wave, in flight
+  // together with Q (all already in flight when the previous tile prefetched
+  // them), so that the first PV does not wait for V_0
+  static_assert(S == 2, "the prologue and the prefetch load two stages' first tiles");
   if (!pre) {
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t)
-#pragma unroll
-      for (int i = 0; i < C::LOADS; ++i) {
-        const int slot = 1024 * (wave + 8 * i);
-        if (t < T) dma16(rk, kring + t * C::TILE + slot, kld[i] + (uint32_t)t * tile_bytes);
-        if (t < S - 2 && t < T) dma16(rv, vring + t * C::TILE + slot, vld[i] + (uint32_t)t * tile_bytes);
-      }
+    for (int i = 0; i < C::LOADS; ++i)
+      if (T > 0) dma16_at(rk, kr + 1024 * (wave + 8 * i), kld[i]);
+    load_tiles(0, slot_off(S - 1), slot_off(S - 2));
   }
   wait_own_loads();
   block_sync();
-  if (group == 1) {
-    // group 1's share of batch 0 goes out with group 0's, at half-phase 0
-    load_tiles(0, slot_off(S - 1), slot_off(S - 2));
-    block_sync();
-  }
+  if (group == 1) block_sync();  // group 1 runs one phase behind
   // Causal: group 0 holds the workgroup's first 128 rows, which see no key of
   // its last tiles (up to two of them). Group 0 runs the full steps only up
   // to the last tile one of its rows can see (Tw), PV of that tile in step
@@ -540,7 +535,6 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // the next tile's Q and first K tile can load now, behind the epilogue.
   bool prefetched = false;
   if (nbh >= 0) {
-    static_assert(S == 2, "the prefetch loads the prologue of two stages: K_0");
     const Slice sn = slice_of(nbh, H, D, Nq_dense, Nk_dense, nullptr, cu_k, total_q, total_k);
     const int q0n = nqt * BM, qin = q0n + rw * 32 + l32;
     const bool ok = qin < sn.Nq;
@@ -550,11 +544,24 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       const u32x4 w = ok ? *(const u32x4*)(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
       qf[s] = __builtin_bit_cast(bf16x8, w);
     }
+    // its prologue's tiles: K_0, then batch 0 (K_1, V_0)
     const int kendn = CAUSAL ? min(sn.Nk, q0n + BM + diag) : sn.Nk;
-    if (kendn > 0) {
-      const u32x4 rkn = raw_buffer_rsrc(K + sn.kbase, (uint32_t)(sn.Nk * rsb));
+    const int Tn = (kendn + BN - 1) / BN;
+    const uint32_t nrecn = (uint32_t)(sn.Nk * rsb);
+    const u32x4 rkn = raw_buffer_rsrc(K + sn.kbase, nrecn);
+    const u32x4 rvn = raw_buffer_rsrc(V + sn.kbase, nrecn);
+    if (Tn > 0) {
 #pragma unroll
-      for (int i = 0; i < C::LOADS; ++i) dma16(rkn, kring + 1024 * (wave + 8 * i), kld[i]);
+      for (int i = 0; i < C::LOADS; ++i) dma16_at(rkn, kr + 1024 * (wave + 8 * i), kld[i]);
+    }
+    if (Tn > 1) {
+      const u32x4 r1 = advance_rsrc(rkn, tile_bytes);
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) dma16_at(r1, kr + C::TILE + 1024 * (wave + 8 * i), kld[i]);
+    }
+    if (Tn > 0) {
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) dma16_at(rvn, vbase + 1024 * (wave + 8 * i), vld[i]);
     }
     prefetched = true;
   }
