@@ -57,11 +57,11 @@ DEFAULT_WORKLOAD = "bf16_b4h16_n4096_d128"
 # it off.
 TRAFFIC = {
     "bf16_b4h16_n4096_d128": {
-        "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "8d0fb6013d42518e",
+        "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "2cf0f9c0887dc927",
                     "online_softmax_fwd_amd/csrc/attn_fwd_bf16_kernels.h": "ed434fc3a23e1aa4",
                     "online_softmax_fwd_amd/csrc/attn_device.h": "16bf28b574555d97",
                     "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "1249699229bb3642"},
-        "fetch_kib_raw": 98467.5, "fetch_scale": 2.0,
+        "fetch_kib_raw": 98475.0, "fetch_scale": 2.0,
         "write_kib_raw": 66560.0, "write_scale": 1.0,
     },
     "mxfp8_b2h16_n8192_d128": {
