@@ -59,17 +59,17 @@ TRAFFIC = {
     "bf16_b4h16_n4096_d128": {
         "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_bf16.hip": "2cf0f9c0887dc927",
                     "online_softmax_fwd_amd/csrc/attn_fwd_bf16_kernels.h": "ed434fc3a23e1aa4",
-                    "online_softmax_fwd_amd/csrc/attn_device.h": "16bf28b574555d97",
+                    "online_softmax_fwd_amd/csrc/attn_device.h": "29e06bec4380ef33",
                     "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "1249699229bb3642"},
-        "fetch_kib_raw": 98475.0, "fetch_scale": 2.0,
+        "fetch_kib_raw": 98476.0, "fetch_scale": 2.0,
         "write_kib_raw": 66560.0, "write_scale": 1.0,
     },
     "mxfp8_b2h16_n8192_d128": {
         "sources": {"online_softmax_fwd_amd/csrc/attn_fwd_mxfp8.hip": "280fe15064e37a4a",
                     "online_softmax_fwd_amd/csrc/attn_mx_common.h": "3ff9393404d4e1ce",
-                    "online_softmax_fwd_amd/csrc/attn_device.h": "16bf28b574555d97",
+                    "online_softmax_fwd_amd/csrc/attn_device.h": "29e06bec4380ef33",
                     "online_softmax_fwd_amd/csrc/attn_bf16_common.h": "1249699229bb3642"},
-        "fetch_kib_raw": 53567.2, "fetch_scale": 2.0,
+        "fetch_kib_raw": 53544.7, "fetch_scale": 2.0,
         "write_kib_raw": 66560.0, "write_scale": 1.0,
     },
 }

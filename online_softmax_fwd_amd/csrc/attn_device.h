@@ -207,7 +207,9 @@ __device__ __forceinline__ void causal_tile_of(int wg, int n_wg, int n_qt, int& 
 // wave waits on its vector-memory counter (s_waitcnt vmcnt) before the
 // workgroup barrier that precedes the reads, and no DMA targets a buffer
 // before the barrier after its last read. The asm sets M0 itself; no compiler
-// builtin that depends on M0 runs in these kernels.
+// builtin that depends on M0 runs in these kernels. An SALU write of M0 needs
+// one wait state before an LDS DMA reads it (the compiler puts the same s_nop
+// between the two for its own LDS-DMA builtins on gfx950), hence the s_nop.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 raw_buffer_rsrc(const void* base, uint32_t nbytes) {
   const uint64_t p = (uint64_t)base;
@@ -218,12 +220,12 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 }
 __device__ __forceinline__ void dma16(const u32x4& rs, const char* lds, uint32_t off) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(rs)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(rs)
                : "memory");
 }
 // The same with the LDS destination as a wave-uniform 32-bit LDS address.
 __device__ __forceinline__ void dma16_at(const u32x4& rs, uint32_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(off), "s"(rs)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(off), "s"(rs)
                : "memory");
 }
 // The raw buffer descriptor rs moved off bytes forward: the base advances
